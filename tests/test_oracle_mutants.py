@@ -1,0 +1,58 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+in tests/test_oracle_pins.py catch every one of them.
+
+Each mutant is a one-line edit of oracle/oracle.c (a dropped term, a flipped
+sign, a wrong index or divisor, a swapped operand), compiled on the CPU into a
+temporary library; the pin suite is run against it in a child process and
+must fail. The oracle source in the repository is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "eps_dropped": ("sumsq / (double)N + eps", "sumsq / (double)N"),
+    "rstd_not_inverted": ("r = 1.0 / sqrt(", "r = sqrt("),
+    "forward_gamma_dropped": ("* r * up(gamma, dtype, j);", "* r;"),
+    "c1_divisor_n_minus_1": ("c1 /= (double)N;", "c1 /= (double)(N > 1 ? N - 1 : 1);"),
+    "c1_not_divided": ("c1 /= (double)N;", ""),
+    "dx_sign_flipped": ("dx_row[j] = (wdy - x_hat * c1) * r;", "dx_row[j] = (wdy + x_hat * c1) * r;"),
+    "dx_c1_term_dropped": ("dx_row[j] = (wdy - x_hat * c1) * r;", "dx_row[j] = wdy * r;"),
+    "dx_final_rstd_dropped": ("dx_row[j] = (wdy - x_hat * c1) * r;", "dx_row[j] = wdy - x_hat * c1;"),
+    "dgamma_uses_wdy": ("dgamma[j] += dyj * x_hat;", "dgamma[j] += wdy * x_hat;"),
+    "dgamma_uses_x": ("dgamma[j] += dyj * x_hat;", "dgamma[j] += dyj * up(x, dtype, row * N + j);"),
+    "gamma_wrong_index": ("double wdy = up(dy, dtype, row * N + j) * up(gamma, dtype, j);",
+                          "double wdy = up(dy, dtype, row * N + j) * up(gamma, dtype, (j + row) % N);"),
+    "x_hat_reads_dy": ("double x_hat = up(x, dtype, row * N + j) * r;\n        double wdy",
+                       "double x_hat = up(dy, dtype, row * N + j) * r;\n        double wdy"),
+    "c1_misses_rstd": ("double x_hat = up(x, dtype, row * N + j) * r;\n        double wdy",
+                       "double x_hat = up(x, dtype, row * N + j);\n        double wdy"),
+    "fused_dres_subtracted": ("d_added[j] += up(dresidual_out", "d_added[j] -= up(dresidual_out"),
+    "fused_sum_is_difference": ("(float)up(x, dtype, k) + (float)up(residual", "(float)up(x, dtype, k) - (float)up(residual"),
+    "encode_ties_away": ("q = (uint64_t)nearbyint(", "q = (uint64_t)round("),
+    "decode_subnormal_scale": ("ldexp((double)m, 1 - bias - f.mbits)", "ldexp((double)m, -bias - f.mbits)"),
+    "decode_bias_off_by_one": ("(int)e - bias - f.mbits)", "(int)e - bias - f.mbits + 1)"),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    msrc = tmp_path / "oracle_mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = str(tmp_path / "liboracle_mutant.so")
+    obuild.build(out=lib, src=str(msrc), extra_flags=["-Wno-error"])
+    env = dict(os.environ, ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
