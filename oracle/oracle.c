@@ -127,13 +127,23 @@ static uint32_t encode_bits(double v, struct fmt f)
     return sbit | (uint32_t)bits;
 }
 
+/* A bf16 pattern is the upper half of the fp32 pattern of the same value, so
+ * widening it is a shift; the same result as decode_bits, much faster. */
+static double up_bf16(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
 /* Exact widening of element i of a typed array to fp64 ("up" in the notes). */
 static double up(const void *p, int dtype, int64_t i)
 {
     switch (dtype) {
     case ORC_F32: return (double)((const float *)p)[i];
     case ORC_F16: return decode_bits(((const uint16_t *)p)[i], FMT_F16);
-    default: return decode_bits(((const uint16_t *)p)[i], FMT_BF16);
+    default: return up_bf16(((const uint16_t *)p)[i]);
     }
 }
 

@@ -38,6 +38,9 @@ MUTANTS = {
     "encode_ties_away": ("q = (uint64_t)nearbyint(", "q = (uint64_t)round("),
     "decode_subnormal_scale": ("ldexp((double)m, 1 - bias - f.mbits)", "ldexp((double)m, -bias - f.mbits)"),
     "decode_bias_off_by_one": ("(int)e - bias - f.mbits)", "(int)e - bias - f.mbits + 1)"),
+    "bf16_widen_shift": ("uint32_t w = (uint32_t)bits << 16;", "uint32_t w = (uint32_t)bits << 15;"),
+    "fused_dres_dropped": ("d_added[j] += up(dresidual_out", "d_added[j] += 0.0 * up(dresidual_out"),
+    "rstd_stored_as_sqrt_ms": ("rstd[row] = (float)r;", "rstd[row] = (float)(1.0 / r);"),
 }
 
 
