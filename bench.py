@@ -1,0 +1,205 @@
+"""Benchmark: rmsnorm_bwd microseconds per call and achieved HBM bandwidth at
+4096 x 4096 bf16, on one MI355X, through the C ABI.
+
+A step is one call of the backward entry point (dx and dgamma, with the dgamma
+finalize and the bf16 cast of dgamma inside the call). Inputs are seeded
+synthetic rows; rstd comes from the library's own forward. By default the
+timed calls rotate over enough buffer sets (> 512 MiB) that no call finds its
+rows in the 256 MiB memory-side cache: every byte comes from HBM. The line
+also carries the hot-cache time (one buffer set, as the pages time it), the
+forward's time, the roofline of the dominant kernel and the CPU oracle's time
+on the same workload.
+
+python bench.py [--steps K] [--warmup W] [--workload NAME] [--hot] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import rmsnorm_bwd_amd as R  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+ROTATE_BYTES = 600 << 20  # > 2 x the 256 MiB memory-side cache
+
+
+def algorithmic_bytes(w):
+    """Bytes the backward must move: read x (or added), dy, [dresidual_out],
+    gamma, rstd; write dx, dgamma_f32 and the dtype copy of dgamma."""
+    s = w.elem_bytes
+    rows = (4 if w.op == "fused" else 3) * w.M * w.N * s
+    return rows + w.N * s + 4 * w.M + 4 * w.N + (w.N * s if s != 4 else 0)
+
+
+def fwd_bytes(w):
+    s = w.elem_bytes
+    rows = (4 if w.op == "fused" else 2) * w.M * w.N * s
+    return rows + w.N * s + 4 * w.M
+
+
+def make_sets(w, d, nsets):
+    """nsets independent device buffer sets holding the same inputs."""
+    dev = torch.device("cuda:0")
+    g = d["gamma"].to(dev)
+    sets = []
+    for _ in range(nsets):
+        if w.op == "plain":
+            x = d["x"].to(dev)
+            y, rstd = R.rmsnorm_fwd_rstd(x, g, w.eps)
+            s = dict(x=x, dy=d["dy"].to(dev), dres=None, rstd=rstd)
+        else:
+            x, res = d["x"].to(dev), d["residual"].to(dev)
+            out, added, rstd = R.fused_add_rmsnorm_fwd_rstd(x, res, g, w.eps)
+            del x, res, out
+            s = dict(x=added, dy=d["dy"].to(dev), dres=d["dresidual_out"].to(dev), rstd=rstd)
+        s["dx"] = torch.empty_like(s["x"])
+        s["dg32"] = torch.empty(w.N, dtype=torch.float32, device=dev)
+        s["dg"] = torch.empty(w.N, dtype=w.torch_dtype, device=dev)
+        s["ws"] = torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(w.M, w.N, w.torch_dtype)),
+                              dtype=torch.uint8, device=dev)
+        sets.append(s)
+    return g, sets
+
+
+def call_bwd(w, g, s):
+    if w.op == "plain":
+        R.rmsnorm_bwd(s["x"], g, s["dy"], s["rstd"], dx=s["dx"], dgamma_f32=s["dg32"],
+                      dgamma=s["dg"], workspace=s["ws"])
+    else:
+        R.fused_add_rmsnorm_bwd(s["x"], g, s["dy"], s["dres"], s["rstd"], dx=s["dx"],
+                                dgamma_f32=s["dg32"], dgamma=s["dg"], workspace=s["ws"])
+
+
+def time_calls(fn, sets, steps, warmup):
+    """Average ms per call over `steps` calls, HIP events on the current stream
+    (the stream every call is launched on), synchronised on both sides."""
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, d, calls=5):
+    """The CPU oracle (fp64, single thread) on the same workload."""
+    import oracle
+    x = d["x"] if w.op == "plain" else None
+    if w.op == "plain":
+        rstd, _ = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps, want_y=False)
+        run = lambda: oracle.rmsnorm_bwd(x, d["gamma"], d["dy"], rstd)  # noqa: E731
+    else:
+        added, rstd, _ = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps,
+                                                      want_out=False)
+        run = lambda: oracle.fused_add_rmsnorm_bwd(added, d["gamma"], d["dy"],  # noqa: E731
+                                                   d["dresidual_out"], rstd)
+    ts = []
+    for _ in range(calls):
+        t0 = time.perf_counter()
+        run()
+        ts.append(time.perf_counter() - t0)
+    us = statistics.median(ts) * 1e6
+    return {"value": round(us, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {calls} calls, median; "
+                      "fp64 C oracle, one thread",
+            "GBps": round(algorithmic_bytes(w) / us / 1e3, 2)}
+
+
+def load_traffic(w):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, when they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    from hashlib import sha256
+    src = b"".join(open(os.path.join(ROOT, "rmsnorm_bwd_amd", "csrc", f), "rb").read()
+                   for f in ("kernels.hip", "device.h", "plan.h", "capi.cpp"))
+    if rec.get("source_sha256") != sha256(src).hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=workloads.HEADLINE)
+    ap.add_argument("--hot", action="store_true", help="time one buffer set only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(dgamma would need one all-reduce per step across GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.WORKLOADS[args.workload]
+    d = workloads.make_inputs(w)
+    per_set = 4 * w.M * w.N * w.elem_bytes
+    nsets = 1 if args.hot else max(2, -(-ROTATE_BYTES // per_set))
+    g, sets = make_sets(w, d, nsets)
+    bwd = lambda s: call_bwd(w, g, s)  # noqa: E731
+    ms = time_calls(bwd, sets, args.steps, args.warmup)
+    ms_hot = ms if args.hot else time_calls(bwd, sets[:1], args.steps, args.warmup)
+
+    def fwd(s):
+        if w.op == "plain":
+            R.rmsnorm_fwd_rstd(s["x"], g, w.eps, y=s["dx"], rstd=s["rstd"])
+        else:
+            R.fused_add_rmsnorm_fwd_rstd(s["x"], s["dy"], g, w.eps, out=s["dx"],
+                                         residual_out=s["dres"], rstd=s["rstd"])
+    ms_fwd = time_calls(fwd, sets, args.steps, args.warmup)
+
+    abytes = algorithmic_bytes(w)
+    gbps = abytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "rmsnorm_bwd us/call + achieved HBM GB/s (% of peak), 4096x4096 bf16",
+        "value": round(ms * 1e3, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "dtype": w.dtype,
+                   "eps": w.eps, "buffer_sets": nsets,
+                   "timing": "hot" if args.hot else "rotated over > 512 MiB"},
+        "achieved_GBps": round(gbps, 1),
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "hot_cache_us": round(ms_hot * 1e3, 2),
+        "fwd_rstd_us": round(ms_fwd * 1e3, 2),
+        "fwd_rstd_GBps": round(fwd_bytes(w) / (ms_fwd * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(w),
+                     "kernel": "one rmsnorm_bwd call (main pass + dgamma finalize)",
+                     "algorithmic_bytes": abytes},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, d)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * rmsnorm_mi355x.h - C ABI of the MI355X (gfx950) RMSNorm library: the
+ * forward passes that save a per-row rstd, and the backward passes (dx and the
+ * weight gradient dgamma), plain and fused-add (prenorm residual).
+ *
+ * Pages cited, by title:
+ *   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
+ *          rstd) to enable training / downstream (quack) integration"
+ *   [P800] FlyDSL PR #800, "[rmsnorm] Add fused-add / residual backward
+ *          (PR 2/3, #769)"
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer on the calling thread's current
+ *     HIP device. The caller owns every buffer, the workspace included. The
+ *     library allocates nothing, frees nothing and never synchronises.
+ *   - Row tensors are (M, N), row-major and contiguous (row stride N
+ *     elements); gamma and the dgamma outputs have N elements; rstd has M.
+ *   - One element dtype (rmsn_dtype_t) covers every row tensor and gamma.
+ *     rstd and dgamma_f32 are always float32.
+ *   - Pointers need only element alignment. Rows whose start is not 16-byte
+ *     aligned, or N that is not a multiple of the 16-byte vector, take a
+ *     slower element-wise path with identical results.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the null stream). A status of RMSN_OK means the launch was enqueued.
+ *   - Arguments are validated before anything is enqueued; a rejected call
+ *     writes nothing. Inputs and outputs must not overlap, except where an
+ *     entry point says so.
+ *   - Limits: 0 <= M <= 2^31 - 1, 1 <= N <= RMSN_MAX_N.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMSN_MAX_N 16384
+
+typedef enum { RMSN_F32 = 0, RMSN_F16 = 1, RMSN_BF16 = 2 } rmsn_dtype_t;
+
+typedef enum {
+    RMSN_OK = 0,
+    RMSN_ERR_NULL = 1,      /* a required pointer is NULL */
+    RMSN_ERR_SHAPE = 2,     /* M < 0, M too large, N < 1 or N > RMSN_MAX_N */
+    RMSN_ERR_DTYPE = 3,     /* unknown dtype code */
+    RMSN_ERR_EPS = 4,       /* eps is negative, NaN or infinite */
+    RMSN_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query */
+    RMSN_ERR_FLAGS = 6,     /* unknown or contradictory flag bits */
+    RMSN_ERR_DEVICE = 7,    /* a pointer is not on the current device */
+    RMSN_ERR_HIP = 8,       /* the HIP runtime reported an error */
+    RMSN_ERR_ALIGN = 9      /* a pointer is not aligned to its element size */
+} rmsn_status_t;
+
+/* Flags of the backward entry points. How dgamma's per-workgroup fp32
+ * partials are combined across workgroups:
+ *   RMSN_DGAMMA_AUTO           the library's measured default;
+ *   RMSN_DGAMMA_DETERMINISTIC  partials go to the workspace and a second
+ *                              kernel sums them in a fixed order: the same
+ *                              inputs give the same bits on every call;
+ *   RMSN_DGAMMA_ATOMIC         partials are added with fp32 atomics into the
+ *                              workspace; the sum order, so the last bits of
+ *                              dgamma, may vary from call to call.
+ * RMSN_CHECK_DEVICE additionally checks, with the HIP runtime, that every
+ * pointer belongs to the current device (the fault the pages' device guard
+ * fixed: [P800] review-fix commit). */
+enum {
+    RMSN_DGAMMA_AUTO = 0,
+    RMSN_DGAMMA_DETERMINISTIC = 1,
+    RMSN_DGAMMA_ATOMIC = 2,
+    RMSN_CHECK_DEVICE = 4
+};
+
+/* RMSNorm forward that also saves rstd.
+ * [I769] Scope/tasks, item 2, and Implementation plan (PR 1): the forward
+ * already forms rrms = rsqrt(mean(x^2) + eps) per row; it now also stores it.
+ * [P800] PR-1 commit: rstd is 1/RMS, fp32, shape (M,); eps is honoured
+ * (review-fix commit).
+ *   y[i,j]  = x[i,j] * rstd[i] * gamma[j], rounded once to the dtype
+ *   rstd[i] = 1 / sqrt(sum_j x[i,j]^2 / N + eps), fp32
+ * In: x (M,N), gamma (N). Out: y (M,N), rstd (M). eps >= 0 and finite. */
+int rmsnorm_fwd_rstd(const void *x, const void *gamma, void *y, float *rstd,
+                     int64_t M, int64_t N, float eps, int dtype, void *stream);
+
+/* Fused-add (prenorm) forward that saves rstd. [P800] fused-add commit and
+ * PR body: added = x + residual is returned as residual_out, normalised into
+ * out, and its per-row rstd is saved.
+ *   residual_out[i,j] = x[i,j] + residual[i,j] (fp32 sum, one rounding)
+ *   rstd and out as in rmsnorm_fwd_rstd, taken over residual_out as stored.
+ * In: x, residual (M,N), gamma (N). Out: out, residual_out (M,N), rstd (M).
+ * residual_out may be the same buffer as residual (in-place update); no other
+ * overlap is allowed. */
+int fused_add_rmsnorm_fwd_rstd(const void *x, const void *residual, const void *gamma,
+                               void *out, void *residual_out, float *rstd,
+                               int64_t M, int64_t N, float eps, int dtype, void *stream);
+
+/* Bytes of device workspace the backward entry points need for (M, N, dtype,
+ * flags). The answer never exceeds 256 + 256 * N * 4 bytes. The caller allocates at least this much, 256-byte aligned, and passes it to
+ * rmsnorm_bwd / fused_add_rmsnorm_bwd. Returns 0 for arguments the backward
+ * would reject. Makes no HIP call. */
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags);
+
+/* RMSNorm backward. [I769] Implementation plan, Math; [P800] PR-1 commit:
+ * with x_hat = x * rstd and wdy = dy * gamma, per row
+ *   c1       = (1/N) sum_j x_hat[j] * wdy[j]            (fp32)
+ *   dx[i,j]  = (wdy[j] - x_hat[j] * c1) * rstd[i]        (rounded once)
+ *   dgamma_f32[j] = sum_i dy[i,j] * x_hat[i,j]           (fp32, over all M rows)
+ *   dgamma[j] = dgamma_f32[j] rounded to the dtype (only if dgamma != NULL)
+ * In: x, dy (M,N); gamma (N); rstd (M, fp32, as saved by a forward).
+ * Out: dx (M,N); dgamma_f32 (N, fp32, overwritten: the caller does not
+ * zero it); dgamma (N, dtype, nullable). With M = 0, dgamma is all zeros.
+ * workspace: device memory of at least rmsnorm_bwd_workspace_bytes(M, N,
+ * dtype, flags) bytes, 256-byte aligned, for this call's exclusive use until
+ * the call's work on `stream` completes; its contents on entry do not
+ * matter. flags: one RMSN_DGAMMA_* mode, optionally | RMSN_CHECK_DEVICE. */
+int rmsnorm_bwd(const void *x, const void *gamma, const void *dy, const float *rstd,
+                void *dx, float *dgamma_f32, void *dgamma,
+                void *workspace, size_t workspace_bytes,
+                int64_t M, int64_t N, int dtype, unsigned flags, void *stream);
+
+/* Fused-add (prenorm) RMSNorm backward. [P800] fused-add commit and PR body:
+ * the plain backward taken over added (= residual_out of the forward), plus
+ * the gradient arriving at residual_out:
+ *   dx[i,j] = (wdy[j] - a_hat[j] * c1) * rstd[i] + dresidual_out[i,j]
+ * Because added = x + residual, this one tensor is both the gradient of x
+ * and of residual: it is stored once and the caller uses it for both.
+ * dresidual_out may be NULL, which stands for zeros. dgamma is the plain
+ * backward's dgamma over added. Other arguments as in rmsnorm_bwd. */
+int fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *dy,
+                          const void *dresidual_out, const float *rstd,
+                          void *dx, float *dgamma_f32, void *dgamma,
+                          void *workspace, size_t workspace_bytes,
+                          int64_t M, int64_t N, int dtype, unsigned flags, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *rmsn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */

@@ -1,0 +1,216 @@
+// capi.cpp - the library's C ABI: argument validation (before any HIP call),
+// launch planning, and dispatch to the kernels on the caller's stream.
+//
+// Pages cited, by title:
+//   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
+//          rstd) to enable training / downstream (quack) integration"
+//   [P800] FlyDSL PR #800, "[rmsnorm] Add fused-add / residual backward
+//          (PR 2/3, #769)" - review-fix commit (shape/contiguity checks,
+//          device guard) and fused-add commit (one dtype for all operands).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "launch.h"
+#include "plan.h"
+#include "rmsnorm_mi355x.h"
+
+namespace {
+
+using rmsn::RowPlan;
+
+bool dtype_ok(int d) { return d == RMSN_F32 || d == RMSN_F16 || d == RMSN_BF16; }
+int esize(int d) { return d == RMSN_F32 ? 4 : 2; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int64_t M, int64_t N) {
+    if (M < 0 || M > INT32_MAX || N < 1 || N > RMSN_MAX_N) return RMSN_ERR_SHAPE;
+    return RMSN_OK;
+}
+
+int check_eps(float eps) {
+    if (!(eps >= 0.0f) || std::isinf(eps)) return RMSN_ERR_EPS;
+    return RMSN_OK;
+}
+
+int check_flags(unsigned flags) {
+    if (flags & ~7u) return RMSN_ERR_FLAGS;
+    if ((flags & 3u) == 3u) return RMSN_ERR_FLAGS;  // deterministic and atomic at once
+    return RMSN_OK;
+}
+
+bool all_aligned(std::initializer_list<const void *> ptrs, uintptr_t a) {
+    for (const void *p : ptrs)
+        if (p && !aligned(p, a)) return false;
+    return true;
+}
+
+// The pointer-only checks the pages' device guard stood for: each non-null
+// pointer must be device memory of the current device.
+int check_device(std::initializer_list<const void *> ptrs) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return RMSN_ERR_HIP;
+    }
+    for (const void *p : ptrs) {
+        if (!p) continue;
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return RMSN_ERR_DEVICE;
+        }
+        if (attr.type != hipMemoryTypeDevice || attr.device != dev) return RMSN_ERR_DEVICE;
+    }
+    return RMSN_OK;
+}
+
+// dgamma mode actually run: a single block writes dgamma itself; otherwise
+// the requested mode, with AUTO resolving to the deterministic two-stage sum.
+int resolve_mode(unsigned flags, int64_t grid) {
+    if (grid <= 1) return rmsn::DG_DIRECT;
+    if ((flags & 3u) == RMSN_DGAMMA_ATOMIC) return rmsn::DG_ATOMIC;
+    return rmsn::DG_PARTIAL;
+}
+
+size_t workspace_for(int64_t M, int64_t N, int dtype, unsigned flags, bool vector_ok) {
+    RowPlan p;
+    if (!rmsn::plan_rows(N, esize(dtype), vector_ok, &p)) return 0;
+    int64_t grid = rmsn::bwd_blocks(M, p);
+    return rmsn::bwd_workspace(M, N, p, resolve_mode(flags, grid));
+}
+
+int bwd_common(const void *x, const void *gamma, const void *dy, const void *dres, const float *rstd,
+               void *dx, float *dgamma_f32, void *dgamma, void *workspace, size_t workspace_bytes,
+               int64_t M, int64_t N, int dtype, unsigned flags, void *stream) {
+    if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
+    if (int st = check_shape(M, N)) return st;
+    if (int st = check_flags(flags)) return st;
+    if (!gamma || !dgamma_f32 || !workspace) return RMSN_ERR_NULL;
+    if (M > 0 && (!x || !dy || !rstd || !dx)) return RMSN_ERR_NULL;
+    const int es = esize(dtype);
+    if (!all_aligned({x, gamma, dy, dres, dx, dgamma}, es) || !all_aligned({rstd, dgamma_f32}, 4) ||
+        !aligned(workspace, 256))
+        return RMSN_ERR_ALIGN;
+    const bool vector_ok = all_aligned({x, gamma, dy, dres, dx}, 16);
+    RowPlan p;
+    if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
+    const int64_t grid = rmsn::bwd_blocks(M, p);
+    const int mode = resolve_mode(flags, grid);
+    // the public query's answer, whatever plan the pointers select, so a
+    // buffer sized by the query is always accepted and nothing less is
+    if (workspace_bytes < rmsnorm_bwd_workspace_bytes(M, N, dtype, flags)) return RMSN_ERR_WORKSPACE;
+    if (flags & RMSN_CHECK_DEVICE) {
+        if (int st = check_device({x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace})) return st;
+    }
+    rmsn::BwdArgs a;
+    a.x = x;
+    a.gamma = gamma;
+    a.dy = dy;
+    a.dres = dres;
+    a.rstd = rstd;
+    a.dx = dx;
+    a.partials = nullptr;
+    a.dgamma_f32 = dgamma_f32;
+    a.dgamma = dgamma;
+    a.M = M;
+    a.N = (int)N;
+    a.mode = mode;
+    hipError_t e = rmsn::launch_bwd(dtype, p, a, (int)grid, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP;
+}
+
+// Blocks for the forward: enough to fill the chip several times over; each
+// block walks rows with a stride, so any M is covered.
+int64_t fwd_blocks(int64_t M, const RowPlan &p) {
+    int64_t steps = (M + p.rpb - 1) / p.rpb;
+    const int64_t cap = 2048;
+    if (steps < 1) steps = 1;
+    return steps < cap ? steps : cap;
+}
+
+int fwd_common(const void *x, const void *residual, const void *gamma, void *y, void *residual_out,
+               float *rstd, int64_t M, int64_t N, float eps, int dtype, void *stream, bool fused) {
+    if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
+    if (int st = check_shape(M, N)) return st;
+    if (int st = check_eps(eps)) return st;
+    if (!gamma) return RMSN_ERR_NULL;
+    if (M > 0 && (!x || !y || !rstd)) return RMSN_ERR_NULL;
+    if (fused && M > 0 && (!residual || !residual_out)) return RMSN_ERR_NULL;
+    const int es = esize(dtype);
+    if (!all_aligned({x, residual, gamma, y, residual_out}, es) || !all_aligned({rstd}, 4))
+        return RMSN_ERR_ALIGN;
+    const bool vector_ok = all_aligned({x, residual, gamma, y, residual_out}, 16);
+    RowPlan p;
+    if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
+    rmsn::FwdArgs a;
+    a.x = x;
+    a.residual = fused ? residual : nullptr;
+    a.gamma = gamma;
+    a.y = y;
+    a.residual_out = fused ? residual_out : nullptr;
+    a.rstd = rstd;
+    a.M = M;
+    a.N = (int)N;
+    a.eps = eps;
+    hipError_t e = rmsn::launch_fwd(dtype, p, a, (int)fwd_blocks(M, p), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmsnorm_fwd_rstd(const void *x, const void *gamma, void *y, float *rstd, int64_t M, int64_t N, float eps,
+                     int dtype, void *stream) {
+    return fwd_common(x, nullptr, gamma, y, nullptr, rstd, M, N, eps, dtype, stream, false);
+}
+
+int fused_add_rmsnorm_fwd_rstd(const void *x, const void *residual, const void *gamma, void *out,
+                               void *residual_out, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+                               void *stream) {
+    return fwd_common(x, residual, gamma, out, residual_out, rstd, M, N, eps, dtype, stream, true);
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags) {
+    if (!dtype_ok(dtype) || check_shape(M, N) || check_flags(flags)) return 0;
+    // alignment is not known here: answer for whichever row plan needs more
+    size_t a = workspace_for(M, N, dtype, flags, true);
+    size_t b = workspace_for(M, N, dtype, flags, false);
+    return a > b ? a : b;
+}
+
+int rmsnorm_bwd(const void *x, const void *gamma, const void *dy, const float *rstd, void *dx,
+                float *dgamma_f32, void *dgamma, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                int dtype, unsigned flags, void *stream) {
+    return bwd_common(x, gamma, dy, nullptr, rstd, dx, dgamma_f32, dgamma, workspace, workspace_bytes, M, N,
+                      dtype, flags, stream);
+}
+
+int fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *dy, const void *dresidual_out,
+                          const float *rstd, void *dx, float *dgamma_f32, void *dgamma, void *workspace,
+                          size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
+                          void *stream) {
+    return bwd_common(added, gamma, dy, dresidual_out, rstd, dx, dgamma_f32, dgamma, workspace,
+                      workspace_bytes, M, N, dtype, flags, stream);
+}
+
+const char *rmsn_status_string(int status) {
+    switch (status) {
+    case RMSN_OK: return "ok";
+    case RMSN_ERR_NULL: return "a required pointer is NULL";
+    case RMSN_ERR_SHAPE: return "M or N out of range";
+    case RMSN_ERR_DTYPE: return "unknown dtype";
+    case RMSN_ERR_EPS: return "eps must be finite and >= 0";
+    case RMSN_ERR_WORKSPACE: return "workspace missing or too small";
+    case RMSN_ERR_FLAGS: return "unknown or contradictory flags";
+    case RMSN_ERR_DEVICE: return "pointer is not on the current device";
+    case RMSN_ERR_HIP: return "HIP runtime error";
+    case RMSN_ERR_ALIGN: return "pointer not aligned to its element size";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// device.h - gfx950 device helpers: element traits with packed loads/stores,
+// round-to-nearest-even output conversion, and cross-lane sums built on DPP,
+// ds_swizzle and v_readlane (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT> struct ElemSize { static constexpr int value = DT == DT_F32 ? 4 : 2; };
+
+// Raw storage for VEC elements of dtype DT, loaded with one instruction:
+// 16 bytes -> global_load_dwordx4, 8 -> dwordx2, 4 -> dword, 2 -> ushort.
+template <int BYTES> struct RawBits;
+template <> struct RawBits<16> { using type = u32x4; };
+template <> struct RawBits<8> { using type = u32x2; };
+template <> struct RawBits<4> { using type = uint32_t; };
+template <> struct RawBits<2> { using type = uint16_t; };
+
+template <int DT, int VEC> struct Pack {
+    static constexpr int BYTES = VEC * ElemSize<DT>::value;
+    using raw_t = typename RawBits<BYTES>::type;
+    raw_t v;
+};
+
+// 32-bit word w of a raw pack (w < BYTES/4), or the zero-extended 16-bit
+// element for 2-byte packs.
+template <int DT, int VEC>
+__device__ __forceinline__ uint32_t word(const Pack<DT, VEC> &p, int w) {
+    if constexpr (Pack<DT, VEC>::BYTES >= 8) {
+        return p.v[w];
+    } else {
+        return (uint32_t)p.v;
+    }
+}
+
+// Element e of a pack, widened exactly to fp32.
+template <int DT, int VEC>
+__device__ __forceinline__ float elem(const Pack<DT, VEC> &p, int e) {
+    if constexpr (DT == DT_F32) {
+        return __uint_as_float(word(p, e));
+    } else if constexpr (DT == DT_BF16) {
+        uint32_t w = word(p, e >> 1);
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        uint32_t w = word(p, e >> 1);
+        f16x2 h = __builtin_bit_cast(f16x2, w);
+        return (float)h[e & 1];
+    }
+}
+
+// Round two fp32 values to nearest-even in the dtype and pack them into one
+// 32-bit word (lower element first): v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (DT == DT_BF16) {
+        bf16x2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        f16x2 v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint16_t pack1(float a) {
+    if constexpr (DT == DT_BF16) {
+        return __builtin_bit_cast(uint16_t, (__bf16)a);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)a);
+    }
+}
+
+// Round VEC fp32 values to the dtype (nearest-even) into a raw pack.
+template <int DT, int VEC>
+__device__ __forceinline__ Pack<DT, VEC> make_pack(const float (&f)[VEC]) {
+    Pack<DT, VEC> p;
+    if constexpr (DT == DT_F32) {
+        if constexpr (VEC == 1) {
+            p.v = __float_as_uint(f[0]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) p.v[e] = __float_as_uint(f[e]);
+        }
+    } else if constexpr (VEC == 1) {
+        p.v = pack1<DT>(f[0]);
+    } else if constexpr (VEC == 2) {
+        p.v = pack2<DT>(f[0], f[1]);
+    } else {
+#pragma unroll
+        for (int w = 0; w < VEC / 2; ++w) p.v[w] = pack2<DT>(f[2 * w], f[2 * w + 1]);
+    }
+    return p;
+}
+
+// The value an fp32 number takes once stored in the dtype and read back.
+template <int DT>
+__device__ __forceinline__ float round_trip(float a) {
+    if constexpr (DT == DT_F32) {
+        return a;
+    } else if constexpr (DT == DT_BF16) {
+        return __uint_as_float((uint32_t)pack1<DT>(a) << 16);
+    } else {
+        return (float)(_Float16)a;
+    }
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ Pack<DT, VEC> load_pack(const void *base, int64_t elem_index) {
+    using raw_t = typename Pack<DT, VEC>::raw_t;
+    const raw_t *p = reinterpret_cast<const raw_t *>(
+        static_cast<const char *>(base) + elem_index * ElemSize<DT>::value);
+    Pack<DT, VEC> r;
+    r.v = __builtin_nontemporal_load(p);
+    return r;
+}
+
+// Loads of data reused by every row (gamma) keep the default cache policy.
+template <int DT, int VEC>
+__device__ __forceinline__ Pack<DT, VEC> load_pack_cached(const void *base, int64_t elem_index) {
+    using raw_t = typename Pack<DT, VEC>::raw_t;
+    const raw_t *p = reinterpret_cast<const raw_t *>(
+        static_cast<const char *>(base) + elem_index * ElemSize<DT>::value);
+    Pack<DT, VEC> r;
+    r.v = *p;
+    return r;
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ void store_pack(void *base, int64_t elem_index, const Pack<DT, VEC> &v) {
+    using raw_t = typename Pack<DT, VEC>::raw_t;
+    raw_t *p = reinterpret_cast<raw_t *>(static_cast<char *>(base) + elem_index * ElemSize<DT>::value);
+    __builtin_nontemporal_store(v.v, p);
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ Pack<DT, VEC> zero_pack() {
+    Pack<DT, VEC> p;
+    if constexpr (Pack<DT, VEC>::BYTES >= 8) {
+#pragma unroll
+        for (int w = 0; w < Pack<DT, VEC>::BYTES / 4; ++w) p.v[w] = 0u;
+    } else {
+        p.v = 0;
+    }
+    return p;
+}
+
+// An empty asm statement that claims to rewrite the packs' registers: values
+// derived from them before this point cannot be reused after it, so the
+// compiler recomputes them instead of keeping them live.
+template <int DT, int VEC>
+__device__ __forceinline__ void opaque(Pack<DT, VEC> &a, Pack<DT, VEC> &b) {
+    asm volatile("" : "+v"(a.v), "+v"(b.v));
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums. Every lane of an aligned group of W lanes (W a power of two,
+// 16 <= W <= 64) ends with the group's total. Each lane's order of additions
+// is fixed, so results repeat bit for bit from call to call; for W < 64 lanes
+// of one group may associate the partial sums differently and so differ in
+// the last bit. For W = 64 every lane holds the same value.
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(W == 16 || W == 32 || W == 64, "group width");
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_mov<0x124>(v);  // row_ror:4 inside each 16-lane row
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    if constexpr (W >= 32) {
+        // ds_swizzle, bit mode, xor mask 16 (within 32-lane halves)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    }
+    if constexpr (W == 64) {
+        // both 32-lane halves now hold their half's total; v_readlane_b32
+        // reads each, and every lane adds them in the same order
+        v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    }
+    return v;
+}
+
+}  // namespace rmsn

@@ -1,0 +1,46 @@
+// launch.h - kernel argument blocks and the launchers the C ABI calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace rmsn {
+
+struct BwdArgs {
+    const void *x;       // x, or `added` for the fused variant (M, N)
+    const void *gamma;   // (N)
+    const void *dy;      // (M, N)
+    const void *dres;    // dresidual_out (M, N), or null
+    const float *rstd;   // (M)
+    void *dx;            // (M, N)
+    float *partials;     // [grid][N] fp32 block partials (partial mode), set by the launcher
+    float *dgamma_f32;   // (N)
+    void *dgamma;        // (N) in the dtype, or null
+    int64_t M;
+    int N;
+    int mode;            // DG_DIRECT / DG_PARTIAL / DG_ATOMIC
+};
+
+struct FwdArgs {
+    const void *x;         // (M, N)
+    const void *residual;  // (M, N), or null for the plain forward
+    const void *gamma;     // (N)
+    void *y;               // (M, N)
+    void *residual_out;    // (M, N) when residual is given
+    float *rstd;           // (M)
+    int64_t M;
+    int N;
+    float eps;
+};
+
+// Enqueue the backward on stream s: the main kernel with `grid` blocks, plus
+// the dgamma finalize, zero-fill or cast kernels its mode needs.
+hipError_t launch_bwd(int dtype, const RowPlan &p, const BwdArgs &a, int grid, void *workspace,
+                      hipStream_t s);
+
+// Enqueue the forward on stream s with `grid` blocks.
+hipError_t launch_fwd(int dtype, const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s);
+
+}  // namespace rmsn

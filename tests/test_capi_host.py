@@ -1,0 +1,189 @@
+"""Host-side checks of the C ABI library; no GPU needed and no kernel launched.
+
+- the built library loads and exports every function include/*.h declares;
+- argument validation returns the documented status before any HIP call
+  (each case below breaks exactly one rule, and where a missed check could
+  reach a launch, a second, later-checked rule is broken too, so no case can
+  ever enqueue work on the fake addresses it passes);
+- the workspace query is pure host arithmetic with the documented bounds.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+import rmsnorm_bwd_amd as R
+
+# These cases hand the library fake device addresses that validation must
+# refuse. They only run where no GPU is visible, so that a validation gap can
+# never turn into a launch on those addresses.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake-address validation cases run on GPU-less hosts only")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, DTYPE, EPS, WORKSPACE, FLAGS, DEVICE, HIP, ALIGN = range(10)
+A = 0x10000          # a 256-byte-aligned fake device address
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\(([^;{}]*)\)\s*;", text):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"rmsnorm_fwd_rstd", "rmsnorm_bwd", "fused_add_rmsnorm_fwd_rstd",
+            "fused_add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+            "rmsn_status_string"} <= set(names)
+    lib = ctypes.CDLL(R.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings():
+    for s in range(10):
+        assert R.status_string(s) and R.status_string(s) != "unknown status"
+    assert R.status_string(99) == "unknown status"
+
+
+def bwd(**kw):
+    a = dict(x=A, gamma=A, dy=A, rstd=A, dx=A, dg32=A, dg=None, ws=A, wsb=0,
+             M=4, N=64, dtype=R.BF16, flags=0)
+    a.update(kw)
+    return R.lib().rmsnorm_bwd(P(a["x"]), P(a["gamma"]), P(a["dy"]), P(a["rstd"]), P(a["dx"]),
+                               P(a["dg32"]), P(a["dg"]), P(a["ws"]), a["wsb"], a["M"], a["N"],
+                               a["dtype"], a["flags"], None)
+
+
+def fused_bwd(**kw):
+    a = dict(x=A, gamma=A, dy=A, dres=None, rstd=A, dx=A, dg32=A, dg=None, ws=A, wsb=0,
+             M=4, N=64, dtype=R.BF16, flags=0)
+    a.update(kw)
+    return R.lib().fused_add_rmsnorm_bwd(P(a["x"]), P(a["gamma"]), P(a["dy"]), P(a["dres"]),
+                                         P(a["rstd"]), P(a["dx"]), P(a["dg32"]), P(a["dg"]),
+                                         P(a["ws"]), a["wsb"], a["M"], a["N"], a["dtype"],
+                                         a["flags"], None)
+
+
+def fwd(**kw):
+    a = dict(x=A, gamma=A, y=A, rstd=A, M=0, N=64, eps=1e-5, dtype=R.BF16)
+    a.update(kw)
+    return R.lib().rmsnorm_fwd_rstd(P(a["x"]), P(a["gamma"]), P(a["y"]), P(a["rstd"]), a["M"],
+                                    a["N"], a["eps"], a["dtype"], None)
+
+
+def fused_fwd(**kw):
+    a = dict(x=A, res=A, gamma=A, out=A, res_out=A, rstd=A, M=0, N=64, eps=1e-5, dtype=R.BF16)
+    if "y" in kw:
+        kw["out"] = kw.pop("y")
+    a.update(kw)
+    return R.lib().fused_add_rmsnorm_fwd_rstd(P(a["x"]), P(a["res"]), P(a["gamma"]), P(a["out"]),
+                                              P(a["res_out"]), P(a["rstd"]), a["M"], a["N"],
+                                              a["eps"], a["dtype"], None)
+
+
+# Every backward case leaves wsb = 0 (too small), and WORKSPACE is checked
+# last: a validation gap would surface as WORKSPACE, never as a launch.
+BWD_CASES = [
+    ("bad dtype", dict(dtype=3), DTYPE),
+    ("negative dtype", dict(dtype=-1), DTYPE),
+    ("N = 0", dict(N=0), SHAPE),
+    ("N too large", dict(N=R.MAX_N + 1), SHAPE),
+    ("M < 0", dict(M=-1), SHAPE),
+    ("M too large", dict(M=1 << 31), SHAPE),
+    ("unknown flag", dict(flags=8), FLAGS),
+    ("both dgamma modes", dict(flags=3), FLAGS),
+    ("gamma NULL", dict(gamma=None), NULL),
+    ("dgamma_f32 NULL", dict(dg32=None), NULL),
+    ("workspace NULL", dict(ws=None), NULL),
+    ("x NULL", dict(x=None), NULL),
+    ("dy NULL", dict(dy=None), NULL),
+    ("rstd NULL", dict(rstd=None), NULL),
+    ("dx NULL", dict(dx=None), NULL),
+    ("x misaligned", dict(x=A + 1), ALIGN),
+    ("f32 dx misaligned", dict(dx=A + 2, dtype=R.F32), ALIGN),
+    ("rstd misaligned", dict(rstd=A + 2), ALIGN),
+    ("dgamma misaligned", dict(dg=A + 1), ALIGN),
+    ("workspace not 256-aligned", dict(ws=A + 16), ALIGN),
+    ("workspace too small", dict(wsb=0), WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_validation(name, kw, want):
+    assert bwd(**kw) == want
+    assert fused_bwd(**kw) == want
+
+
+def test_bwd_workspace_one_byte_short():
+    # everything valid except the size: one byte below the query is refused
+    for M, N, dt in ((4096, 4096, R.BF16), (512, 3000, R.F32), (8, 256, R.F32)):
+        need = R.rmsnorm_bwd_workspace_bytes(M, N, dt)
+        assert bwd(M=M, N=N, dtype=dt, wsb=need - 1) == WORKSPACE
+
+
+def test_fused_bwd_dres_misaligned():
+    assert fused_bwd(dres=A + 1) == ALIGN
+
+
+# Forward cases use M = 0 where they can (nothing is launched for no rows);
+# the M > 0 cases also misalign y, which is checked after the NULL checks.
+FWD_CASES = [
+    ("bad dtype", dict(dtype=5), DTYPE),
+    ("N = 0", dict(N=0), SHAPE),
+    ("N too large", dict(N=R.MAX_N + 1), SHAPE),
+    ("M < 0", dict(M=-3), SHAPE),
+    ("eps NaN", dict(eps=float("nan")), EPS),
+    ("eps negative", dict(eps=-1e-6), EPS),
+    ("eps infinite", dict(eps=float("inf")), EPS),
+    ("gamma NULL", dict(gamma=None), NULL),
+    ("gamma misaligned", dict(gamma=A + 1), ALIGN),
+    ("x NULL", dict(M=2, x=None, y=A + 1), NULL),
+    ("y NULL", dict(M=2, y=None, x=A + 1), NULL),
+    ("rstd NULL", dict(M=2, rstd=None, y=A + 1), NULL),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_fwd_validation(name, kw, want):
+    assert fwd(**kw) == want
+    assert fused_fwd(**kw) == want
+
+
+def test_fused_fwd_needs_residual():
+    assert fused_fwd(M=2, res=None, out=A + 1) == NULL
+    assert fused_fwd(M=2, res_out=None, out=A + 1) == NULL
+
+
+def test_fwd_with_no_rows_is_ok_without_a_launch():
+    assert fwd(M=0) == OK
+    assert fused_fwd(M=0) == OK
+
+
+def test_workspace_query():
+    q = R.rmsnorm_bwd_workspace_bytes
+    assert q(4, 0, R.BF16) == 0 and q(4, 64, 9) == 0 and q(-1, 64, R.BF16) == 0
+    assert q(4, 64, R.BF16, flags=3) == 0
+    # a single block writes dgamma itself: header only
+    assert q(1, 4096, R.BF16) == 256
+    assert q(0, 4096, R.BF16) == 256
+    # many rows: one fp32 partial row per block (at most 256 blocks), in the
+    # deterministic and the default mode; the atomic mode needs none
+    assert q(4096, 4096, R.BF16) == 256 + 256 * 4096 * 4
+    assert q(4096, 4096, R.BF16, R.DGAMMA_DETERMINISTIC) == 256 + 256 * 4096 * 4
+    assert q(4096, 4096, R.BF16, R.DGAMMA_ATOMIC) == 256
+    for M in (1, 7, 100, 5000, 1 << 20):
+        for N in (1, 3, 255, 3000, 4096, 16384):
+            for dt in (R.F32, R.F16, R.BF16):
+                v = q(M, N, dt)
+                assert 256 <= v <= 256 + 256 * N * 4

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the
+seeded workloads (full sizes) and on edge cases: ragged and odd N, one row,
+no rows, misaligned pointers, fp16, both dgamma modes, dresidual_out absent
+and present, the fused forward writing residual_out in place.
+
+Math: FlyDSL issue #769 ("[Feature] Add rmsnorm backward (+ forward saves
+rstd) ..."), Implementation plan: Math; FlyDSL PR #800 ("[rmsnorm] Add
+fused-add / residual backward (PR 2/3, #769)"), fused-add commit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_bwd_amd as R
+import workloads
+from parity_util import (DEV, assert_close, check_case, fused_case, place, plain_case, rel,
+                         tol_dgamma)
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------
+# The named workloads at their full sizes
+# --------------------------------------------------------------------------
+
+PLAIN_FULL = ["plain_8x256_f32", "plain_512x3000_f32", "plain_512x2048_bf16",
+              "plain_4096x4096_bf16", "plain_1x4096_bf16"]
+
+
+@pytest.mark.parametrize("name", PLAIN_FULL)
+def test_plain_workload_full(name):
+    _say("case", name)
+    check_case(plain_case(W[name]))
+
+
+def test_fused_workload_1024x8192_full():
+    _say("case fused_1024x8192_bf16")
+    check_case(fused_case(W["fused_1024x8192_bf16"]))
+
+
+@pytest.mark.slow
+def test_fused_workload_32768x8192():
+    """Full-size fused backward at 32768 x 8192 bf16. dgamma is compared in
+    full (the oracle streams all rows); dx on 260 rows spread over the tensor
+    (every 128th row plus the last four), which the oracle computes one by
+    one. The forward is compared on the same rows, residual_out in full."""
+    w = W["fused_32768x8192_bf16"]
+    _say("case", w.name, "generating inputs")
+    d = workloads.make_inputs(w)
+    T, M, N = w.torch_dtype, w.M, w.N
+    added, r_ref, _ = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps,
+                                                    want_out=False)
+    _say("oracle forward done")
+    xg, resg, gg = place(d["x"]), place(d["residual"]), place(d["gamma"])
+    out, res_out, rstd = R.fused_add_rmsnorm_fwd_rstd(xg, resg, gg, w.eps)
+    del xg, resg
+    ag, dyg, dresg = place(added), place(d["dy"]), place(d["dresidual_out"])
+    dgt = torch.empty(N, dtype=T, device=DEV)
+    dx, dg32, dgt = R.fused_add_rmsnorm_bwd(ag, gg, dyg, dresg, r_ref.to(DEV), dgamma=dgt)
+    torch.cuda.synchronize()
+    _say("gpu done")
+    assert torch.equal(res_out.cpu(), added)
+    er = ((rstd.cpu().double() - r_ref.double()).abs() / r_ref.double()).max().item()
+    assert er <= 1e-5
+    _, dg_ref = oracle.fused_add_rmsnorm_bwd(added, d["gamma"], d["dy"], d["dresidual_out"],
+                                             r_ref, want_dx=False)
+    assert rel(dg32, dg_ref) <= tol_dgamma(M)
+    assert torch.equal(dgt.cpu(), dg32.cpu().to(T))
+    rows = torch.cat([torch.arange(0, M, 128), torch.arange(M - 4, M)])
+    sub = {k: d[k][rows].contiguous() for k in ("x", "residual", "dy", "dresidual_out")}
+    a_s, r_s, o_s = oracle.fused_add_rmsnorm_fwd(sub["x"], sub["residual"], d["gamma"], w.eps)
+    assert torch.equal(a_s, added[rows])
+    assert_close("out", out[rows.to(DEV)], o_s, T)
+    dx_s, _ = oracle.fused_add_rmsnorm_bwd(a_s, d["gamma"], sub["dy"], sub["dresidual_out"], r_s,
+                                           want_dgamma=False)
+    assert_close("dx", dx[rows.to(DEV)], dx_s, T)
+
+
+# --------------------------------------------------------------------------
+# Edge cases and the row-plan paths
+# --------------------------------------------------------------------------
+
+EDGE = [
+    # (M, N, dtype): odd and ragged N take the element path; others cover
+    # every vector row plan (16..512 threads per row) and several rows per wave
+    (1, 1, "f32"), (3, 7, "bf16"), (37, 255, "f16"), (5, 3001, "bf16"), (9, 4097, "f32"),
+    (300, 64, "bf16"), (1000, 128, "f32"), (129, 1024, "f16"), (64, 2048, "f16"),
+    (33, 8192, "bf16"), (17, 16384, "bf16"), (6, 16384, "f32"), (2, 12288, "f32"),
+    (1, 16383, "bf16"), (700, 768, "bf16"), (258, 5120, "f16"),
+]
+
+
+@pytest.mark.parametrize("M,N,dt", EDGE)
+def test_plain_edge_shapes(M, N, dt):
+    _say("case plain", M, N, dt)
+    check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-5, seed=M + N)))
+
+
+@pytest.mark.parametrize("M,N,dt", EDGE[::2])
+def test_fused_edge_shapes(M, N, dt):
+    _say("case fused", M, N, dt)
+    check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M * 3 + N)))
+
+
+@pytest.mark.parametrize("M,N,dt", [(64, 4096, "bf16"), (7, 3000, "f32"), (40, 250, "f16")])
+def test_misaligned_pointers_take_the_element_path(M, N, dt):
+    _say("case misaligned", M, N, dt)
+    check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-5), misalign=True))
+    check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-5), misalign=True))
+
+
+@pytest.mark.parametrize("with_dres", [False, True])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_fused_with_and_without_dresidual(with_dres, dt):
+    _say("case fused dres", with_dres, dt)
+    check_case(fused_case(workloads.custom("fused", 96, 1536, dt, 1e-6), with_dres=with_dres))
+
+
+@pytest.mark.parametrize("eps", [1e-5, 1e-6, 1e-2, 0.0])
+def test_eps_is_honoured(eps):
+    _say("case eps", eps)
+    check_case(plain_case(workloads.custom("plain", 64, 512, "f32", eps)))
+
+
+def test_no_rows():
+    _say("case M=0")
+    for op in ("plain", "fused"):
+        N = 64
+        g = torch.randn(N, device=DEV, dtype=torch.bfloat16)
+        x = torch.empty(0, N, device=DEV, dtype=torch.bfloat16)
+        rstd = torch.empty(0, device=DEV)
+        dg32 = torch.full((N,), 7.0, device=DEV)
+        dgt = torch.full((N,), 7.0, device=DEV, dtype=torch.bfloat16)
+        if op == "plain":
+            R.rmsnorm_bwd(x, g, x, rstd, dgamma_f32=dg32, dgamma=dgt)
+            y, r = R.rmsnorm_fwd_rstd(x, g, 1e-5)
+        else:
+            R.fused_add_rmsnorm_bwd(x, g, x, None, rstd, dgamma_f32=dg32, dgamma=dgt)
+            R.fused_add_rmsnorm_fwd_rstd(x, x, g, 1e-5)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dg32) == 0 and torch.count_nonzero(dgt.float()) == 0
+
+
+def test_batched_input_flattens_leading_dims():
+    _say("case 3-D input")
+    w = workloads.custom("plain", 24, 640, "bf16", 1e-5)
+    d = workloads.make_inputs(w)
+    r_ref, _ = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps)
+    x3 = d["x"].view(4, 6, 640).to(DEV)
+    dy3 = d["dy"].view(4, 6, 640).to(DEV)
+    dx, dg32, _ = R.rmsnorm_bwd(x3, d["gamma"].to(DEV), dy3, r_ref.to(DEV))
+    torch.cuda.synchronize()
+    dx_ref, dg_ref = oracle.rmsnorm_bwd(d["x"], d["gamma"], d["dy"], r_ref)
+    assert dx.shape == (4, 6, 640)
+    assert_close("dx", dx.view(24, 640), dx_ref, torch.bfloat16)
+    assert rel(dg32, dg_ref) <= tol_dgamma(24)
+
+
+# --------------------------------------------------------------------------
+# dgamma modes
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["plain_4096x4096_bf16", "plain_512x3000_f32"])
+def test_deterministic_mode_repeats_bit_for_bit(name):
+    _say("case deterministic", name)
+    c = plain_case(W[name], flags=R.DGAMMA_DETERMINISTIC)
+    check_case(c)
+    xg, gg, dyg, rg = c["inputs"]
+    for _ in range(3):
+        dx, dg32, _ = R.rmsnorm_bwd(xg, gg, dyg, rg, flags=R.DGAMMA_DETERMINISTIC)
+        torch.cuda.synchronize()
+        assert torch.equal(dx, c["dx"][0]) and torch.equal(dg32, c["dg32"][0])
+
+
+@pytest.mark.parametrize("name", ["plain_4096x4096_bf16", "plain_512x2048_bf16"])
+def test_atomic_mode_within_tolerance(name):
+    _say("case atomic", name)
+    check_case(plain_case(W[name], flags=R.DGAMMA_ATOMIC))
+
+
+def test_atomic_mode_fused():
+    _say("case atomic fused")
+    check_case(fused_case(W["fused_1024x8192_bf16"], flags=R.DGAMMA_ATOMIC))
+
+
+# --------------------------------------------------------------------------
+# Aliasing, guards and errors
+# --------------------------------------------------------------------------
+
+def test_fused_forward_in_place_residual():
+    _say("case in-place residual_out")
+    w = workloads.custom("fused", 50, 1000, "bf16", 1e-6)
+    d = workloads.make_inputs(w)
+    a_ref, r_ref, o_ref = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps)
+    res = d["residual"].to(DEV)
+    out, res_out, rstd = R.fused_add_rmsnorm_fwd_rstd(d["x"].to(DEV), res, d["gamma"].to(DEV),
+                                                      w.eps, residual_out=res)
+    torch.cuda.synchronize()
+    assert res_out.data_ptr() == res.data_ptr()
+    assert torch.equal(res.cpu(), a_ref)
+    assert_close("out", out, o_ref, torch.bfloat16)
+
+
+def test_dtype_mismatch_is_refused():
+    # the pages' guard: one dtype across operands, else bytes are reinterpreted
+    x = torch.randn(4, 64, device=DEV, dtype=torch.bfloat16)
+    g = torch.ones(64, device=DEV, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        R.rmsnorm_fwd_rstd(x, g, 1e-5)
+    with pytest.raises(TypeError):
+        R.fused_add_rmsnorm_fwd_rstd(x, x.half(), g.bfloat16(), 1e-5)
+    with pytest.raises(ValueError):
+        R.rmsnorm_fwd_rstd(x, torch.ones(63, device=DEV, dtype=torch.bfloat16), 1e-5)
+    with pytest.raises(ValueError):
+        R.rmsnorm_fwd_rstd(x.t(), torch.ones(4, device=DEV, dtype=torch.bfloat16), 1e-5)
+
+
+def test_device_check_flag_refuses_host_memory():
+    N = 256
+    x = torch.randn(4, N, device=DEV)
+    g = torch.ones(N, device=DEV)
+    rstd = torch.ones(4, device=DEV)
+    host_dy = torch.randn(4, N)
+    ws = torch.empty(R.rmsnorm_bwd_workspace_bytes(4, N, R.F32), dtype=torch.uint8, device=DEV)
+    dx = torch.empty_like(x)
+    dg = torch.empty(N, device=DEV)
+    import ctypes
+    st = R.lib().rmsnorm_bwd(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+                             ctypes.c_void_p(host_dy.data_ptr()), ctypes.c_void_p(rstd.data_ptr()),
+                             ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(dg.data_ptr()), None,
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), 4, N, R.F32,
+                             R.CHECK_DEVICE, None)
+    assert st == 7  # RMSN_ERR_DEVICE, nothing launched
+    # with device memory everywhere, the checked call runs
+    dx2, dg2, _ = R.rmsnorm_bwd(x, g, x, rstd, flags=R.CHECK_DEVICE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dx2).all() and torch.isfinite(dg2).all()
