@@ -113,32 +113,64 @@ __device__ __forceinline__ float round_trip(float a) {
     }
 }
 
-template <int DT, int VEC>
-__device__ __forceinline__ Pack<DT, VEC> load_pack(const void *base, int64_t elem_index) {
-    using raw_t = typename Pack<DT, VEC>::raw_t;
-    const raw_t *p = reinterpret_cast<const raw_t *>(
-        static_cast<const char *>(base) + elem_index * ElemSize<DT>::value);
-    Pack<DT, VEC> r;
-    r.v = __builtin_nontemporal_load(p);
-    return r;
+// ---------------------------------------------------------------------------
+// Buffer resources. A raw buffer descriptor (base address, byte range) lives in
+// four SGPRs; loads through it whose offset lies outside the range return zero
+// and stores outside it are dropped, in hardware. The kernels use that range
+// check instead of branches around memory operations: a row chunk past the
+// row end, or a row past the last row, gets an offset outside the range.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Word 3 of a gfx9-family buffer descriptor: 32-bit data format, identity
+// channel selects (the value the CDNA ISA defines for raw byte buffers).
+constexpr int RSRC_WORD3 = 0x00020000;
+// An offset no descriptor range reaches (every range here is below 2^31).
+constexpr uint32_t OOB = 0x80000000u;
+// Cache-policy bits of a buffer access on gfx950: NT marks data streamed once.
+constexpr int AUX_DEFAULT = 0;
+constexpr int AUX_NT = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, RSRC_WORD3);
 }
 
-// Loads of data reused by every row (gamma) keep the default cache policy.
-template <int DT, int VEC>
-__device__ __forceinline__ Pack<DT, VEC> load_pack_cached(const void *base, int64_t elem_index) {
-    using raw_t = typename Pack<DT, VEC>::raw_t;
-    const raw_t *p = reinterpret_cast<const raw_t *>(
-        static_cast<const char *>(base) + elem_index * ElemSize<DT>::value);
-    Pack<DT, VEC> r;
-    r.v = *p;
-    return r;
+template <int DT, int VEC, int AUX>
+__device__ __forceinline__ Pack<DT, VEC> buf_load(rsrc_t r, uint32_t off) {
+    constexpr int B = Pack<DT, VEC>::BYTES;
+    Pack<DT, VEC> p;
+    if constexpr (B == 16) {
+        p.v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    } else if constexpr (B == 8) {
+        p.v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+    } else if constexpr (B == 4) {
+        p.v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+    } else {
+        p.v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+    }
+    return p;
 }
 
-template <int DT, int VEC>
-__device__ __forceinline__ void store_pack(void *base, int64_t elem_index, const Pack<DT, VEC> &v) {
-    using raw_t = typename Pack<DT, VEC>::raw_t;
-    raw_t *p = reinterpret_cast<raw_t *>(static_cast<char *>(base) + elem_index * ElemSize<DT>::value);
-    __builtin_nontemporal_store(v.v, p);
+template <int DT, int VEC, int AUX>
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, const Pack<DT, VEC> &p) {
+    constexpr int B = Pack<DT, VEC>::BYTES;
+    if constexpr (B == 16) {
+        __builtin_amdgcn_raw_buffer_store_b128(p.v, r, off, 0, AUX);
+    } else if constexpr (B == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(p.v, r, off, 0, AUX);
+    } else if constexpr (B == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(p.v, r, off, 0, AUX);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b16(p.v, r, off, 0, AUX);
+    }
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX_DEFAULT));
+}
+
+__device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, AUX_DEFAULT);
 }
 
 template <int DT, int VEC>

@@ -56,15 +56,39 @@ __device__ __forceinline__ float row_sum(float v, float *slots, int parity) {
     }
 }
 
+// Byte address of element `elem` of a tensor, as an integer: window bases may
+// lie past the end of a tensor when the window holds no row (its descriptor
+// range is then empty and nothing is accessed).
+__device__ __forceinline__ const void *at(const void *base, int64_t elem, int es) {
+    return reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(base) + (uintptr_t)(elem * es));
+}
+
+// Rows of the window starting at row wb that exist: min(RPB, M - wb), >= 0.
+template <int RPB>
+__device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
+    const int64_t r = M - wb;
+    return r <= 0 ? 0u : (r >= RPB ? (uint32_t)RPB : (uint32_t)r);
+}
+
 // ---------------------------------------------------------------------------
 // Backward, main pass. [I769] Implementation plan, Math; [P800] PR-1 and
 // fused-add commits. Per row i (x is `added` for the fused variant):
 //   x_hat = x * rstd_i, wdy = dy * gamma, c1 = (1/N) sum_j x_hat * wdy,
 //   dx = (wdy - x_hat * c1) * rstd_i (+ dresidual_out), dgamma += dy * x_hat.
+//
+// Block b owns the row windows b*rpb + t*gridDim*rpb (t = 0, 1, ...), each
+// window rpb consecutive rows, one per row group. A ring of DEPTH windows is
+// in flight: after a window is reduced and stored, its registers receive the
+// loads of the window DEPTH steps ahead. All row traffic goes through buffer
+// descriptors whose range is the window's existing rows, so rows past M and
+// chunks past the row end read as zero and are not stored, without branches;
+// that keeps the compiler's memory-counter waits exact, so a window's use
+// never waits on the loads of the windows behind it.
 // ---------------------------------------------------------------------------
-template <int DT, int VEC, int TPR, int K, int BLOCK>
+template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
+    constexpr int ES = ElemSize<DT>::value;
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
     extern __shared__ float lds[];
@@ -72,17 +96,28 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     float *comb = lds + 2 * RPB * WPR;
 
     const int N = a.N;
+    const int64_t M = a.M;
+    const uint32_t row_bytes = (uint32_t)N * ES;
     const int nchunk = N / VEC;
     const int grp = threadIdx.x / TPR;
     const int lt = threadIdx.x % TPR;
-    const bool has_dres = a.dres != nullptr;
+    const uint32_t goff = (uint32_t)grp * row_bytes;
 
-    // gamma stays resident, packed, for the whole kernel
-    P gp[K];
+    // byte offset of each owned chunk inside a row; chunks past the row end
+    // get an offset outside every descriptor range
+    uint32_t coff[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int c = lt + k * TPR;
-        gp[k] = c < nchunk ? load_pack_cached<DT, VEC>(a.gamma, (int64_t)c * VEC) : zero_pack<DT, VEC>();
+        coff[k] = c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
+    }
+
+    // gamma stays resident, packed, for the whole kernel
+    P gp[K];
+    {
+        const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
+#pragma unroll
+        for (int k = 0; k < K; ++k) gp[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k]);
     }
     float acc[K][VEC];
 #pragma unroll
@@ -90,92 +125,86 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[k][e] = 0.f;
 
-    // Two x/dy row buffers: `cur` is reduced while `nxt` is in flight.
-    // Chunks past the row end keep their zero fill and add nothing.
-    P xc[K], dc[K], xn[K], dn[K], rc[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) xc[k] = dc[k] = xn[k] = dn[k] = rc[k] = zero_pack<DT, VEC>();
-    float r_cur = 0.f, r_nxt = 0.f;
+    P xs[DEPTH][K], ds[DEPTH][K], rs[DEPTH][FUSED ? K : 1];
+    float rr[DEPTH];
 
-    const int64_t M = a.M;
-    const int64_t stride = (int64_t)gridDim.x * RPB;
-    int64_t base = (int64_t)blockIdx.x * RPB;
+    const int64_t wstride = (int64_t)gridDim.x * RPB;
+    const int64_t w0 = (int64_t)blockIdx.x * RPB;
 
-    auto load_row = [&](int64_t row, P (&xv)[K], P (&dv)[K], float &r) {
-        const int64_t off = row * N;
+    auto load_window = [&](int64_t wb, P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float &r) {
+        const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
+        const rsrc_t rx = make_rsrc(at(a.x, wb * N, ES), bytes);
+        const rsrc_t rd = make_rsrc(at(a.dy, wb * N, ES), bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int c = lt + k * TPR;
-            if (c < nchunk) {
-                xv[k] = load_pack<DT, VEC>(a.x, off + (int64_t)c * VEC);
-                dv[k] = load_pack<DT, VEC>(a.dy, off + (int64_t)c * VEC);
-            }
+            xv[k] = buf_load<DT, VEC, AUX_NT>(rx, goff + coff[k]);
+            dv[k] = buf_load<DT, VEC, AUX_NT>(rd, goff + coff[k]);
         }
-        r = a.rstd[row];
+        if constexpr (FUSED) {
+            const rsrc_t rz = make_rsrc(at(a.dres, wb * N, ES), bytes);
+#pragma unroll
+            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_NT>(rz, goff + coff[k]);
+        }
+        const rsrc_t rt = make_rsrc(at(a.rstd, wb, 4), rows_in<RPB>(wb, M) * 4u);
+        r = buf_load_f32(rt, (uint32_t)grp * 4u);
     };
 
-    if (base + grp < M) load_row(base + grp, xc, dc, r_cur);
-    int parity = 0;
-    for (; base < M; base += stride) {
-        const int64_t row = base + grp;
-        const int64_t nrow = row + stride;
-        const bool valid = row < M;
-        // dresidual_out of this row is issued before the next row's x/dy so
-        // that waiting for it does not wait for the prefetch (loads retire in
-        // order)
-        if (has_dres && valid) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int c = lt + k * TPR;
-                if (c < nchunk) rc[k] = load_pack<DT, VEC>(a.dres, row * N + (int64_t)c * VEC);
-            }
-        }
-        if (nrow < M) load_row(nrow, xn, dn, r_nxt);
-
-        const float r = r_cur;
+    // The same arithmetic as the definition, with the per-row factors pulled
+    // out of the per-element work: sum x_hat*wdy = r * sum x*wdy, and
+    // dx = (wdy - x_hat*c1) * r = r*wdy - (r*r*c1)*x.
+    auto process = [&](int64_t wb, P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, int parity) {
         float part = 0.f;
 #pragma unroll
         for (int k = 0; k < K; ++k)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float xh = elem(xc[k], e) * r;
-                const float wdy = elem(dc[k], e) * elem(gp[k], e);
-                part = fmaf(xh, wdy, part);
-            }
-        const float c1 = row_sum<TPR, BLOCK>(part, slots, parity) / (float)N;
-        // Recompute x_hat and wdy from the packed row below instead of keeping
-        // 2 * K * VEC fp32 values live across the sum.
+            for (int e = 0; e < VEC; ++e) part = fmaf(elem(xv[k], e), elem(dv[k], e) * elem(gp[k], e), part);
+        const float c1 = row_sum<TPR, BLOCK>(part, slots, parity) * r / (float)N;
+        const float b = r * r * c1;
+        // Recompute from the packed row below instead of keeping 2 * K * VEC
+        // fp32 values live across the sum.
 #pragma unroll
-        for (int k = 0; k < K; ++k) opaque(xc[k], dc[k]);
+        for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
 
-        if (valid) {
-            const int64_t off = row * N;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int c = lt + k * TPR;
-                if (c < nchunk) {
-                    float o[VEC];
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const float dyv = elem(dc[k], e);
-                        const float xh = elem(xc[k], e) * r;
-                        const float wdy = dyv * elem(gp[k], e);
-                        float d = fmaf(-xh, c1, wdy) * r;
-                        if (has_dres) d += elem(rc[k], e);
-                        o[e] = d;
-                        acc[k][e] = fmaf(dyv, xh, acc[k][e]);
-                    }
-                    store_pack<DT, VEC>(a.dx, off + (int64_t)c * VEC, make_pack<DT, VEC>(o));
-                }
-            }
-        }
+        const rsrc_t rw = make_rsrc(at(a.dx, wb * N, ES), rows_in<RPB>(wb, M) * row_bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            xc[k] = xn[k];
-            dc[k] = dn[k];
+            float o[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float xv_e = elem(xv[k], e);
+                const float dyv = elem(dv[k], e);
+                float d = fmaf(-b, xv_e, r * (dyv * elem(gp[k], e)));
+                if constexpr (FUSED) d += elem(rv[k], e);
+                o[e] = d;
+                acc[k][e] = fmaf(dyv, xv_e * r, acc[k][e]);
+            }
+            buf_store<DT, VEC, AUX_NT>(rw, goff + coff[k], make_pack<DT, VEC>(o));
         }
-        r_cur = r_nxt;
-        parity ^= 1;
+    };
+
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s]);
+    int parity = 0;
+    // Steady state: groups of DEPTH windows that all hold rows, with no branch
+    // in the body, so every wait counts exactly the loads it needs.
+    int64_t base = w0;
+    for (; base + (DEPTH - 1) * wstride < M; base += DEPTH * wstride) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+            const int64_t wb = base + s * wstride;
+            process(wb, xs[s], ds[s], rs[s], rr[s], parity);
+            parity ^= 1;
+            load_window(wb + DEPTH * wstride, xs[s], ds[s], rs[s], rr[s]);
+        }
+    }
+    // The last, partial group (block-uniform test): its rows are already loaded.
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s) {
+        const int64_t wb = base + s * wstride;
+        if (wb < M) {
+            process(wb, xs[s], ds[s], rs[s], rr[s], parity);
+            parity ^= 1;
+        }
     }
 
     // ---- this block's dgamma partial ----
@@ -224,34 +253,40 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Backward, dgamma finalize (deterministic mode): dgamma_f32[j] = sum over the
-// G block partials in a fixed order, and its rounding to the dtype.
-// 64 columns per block, each summed by 4 threads over interleaved partials,
-// then combined in a fixed order.
+// G block partials in a fixed order, and its rounding to the dtype. A block
+// owns 32 adjacent columns (one 128-byte line of each partial row) and 16
+// splits; split w sums partials w, w + 16, ..., issuing all of its loads
+// before the first add, so the kernel waits for memory once. The 16 sums are
+// then added in split order.
 // ---------------------------------------------------------------------------
+constexpr int FIN_COLS = 32;
+constexpr int FIN_SPLIT = 16;
+constexpr int FIN_LOADS = (BWD_MAX_BLOCKS + FIN_SPLIT - 1) / FIN_SPLIT;
+
 template <int DT>
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(const float *__restrict__ partials, int G,
-                                                           int N, float *__restrict__ dgamma_f32,
-                                                           void *__restrict__ dgamma) {
-    __shared__ float red[4][64];
-    const int l = threadIdx.x & 63;
-    const int split = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + l;
-    float s = 0.f;
-    if (col < N) {
-        int gi = split;
-        for (; gi + 12 < G; gi += 16) {
-            const float v0 = partials[(int64_t)gi * N + col];
-            const float v1 = partials[(int64_t)(gi + 4) * N + col];
-            const float v2 = partials[(int64_t)(gi + 8) * N + col];
-            const float v3 = partials[(int64_t)(gi + 12) * N + col];
-            s = (((s + v0) + v1) + v2) + v3;
-        }
-        for (; gi < G; gi += 4) s += partials[(int64_t)gi * N + col];
+__global__ __launch_bounds__(FIN_COLS *FIN_SPLIT) void bwd_finalize_kernel(const float *__restrict__ partials,
+                                                                          int G, int N,
+                                                                          float *__restrict__ dgamma_f32,
+                                                                          void *__restrict__ dgamma) {
+    __shared__ float red[FIN_SPLIT][FIN_COLS];
+    const int l = threadIdx.x % FIN_COLS;
+    const int split = threadIdx.x / FIN_COLS;
+    const int col = blockIdx.x * FIN_COLS + l;
+    float v[FIN_LOADS];
+#pragma unroll
+    for (int i = 0; i < FIN_LOADS; ++i) {
+        const int gi = split + i * FIN_SPLIT;
+        v[i] = (col < N && gi < G) ? partials[(int64_t)gi * N + col] : 0.f;
     }
+    float s = v[0];
+#pragma unroll
+    for (int i = 1; i < FIN_LOADS; ++i) s += v[i];
     red[split][l] = s;
     __syncthreads();
     if (split == 0 && col < N) {
-        const float t = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+        float t = red[0][l];
+#pragma unroll
+        for (int w = 1; w < FIN_SPLIT; ++w) t += red[w][l];
         dgamma_f32[col] = t;
         if (dgamma) {
             if constexpr (DT == DT_F32) {
@@ -285,92 +320,113 @@ __global__ __launch_bounds__(256) void cast_kernel(const float *__restrict__ src
 // commit (added = x + residual is residual_out, rstd is that of added).
 //   a = x, or round(x + residual) for the fused variant (fp32 sum, one RNE)
 //   rstd = 1 / sqrt(sum a^2 / N + eps);   y = a * rstd * gamma
+// Same windows, ring and buffer descriptors as the backward.
 // ---------------------------------------------------------------------------
-template <int DT, int VEC, int TPR, int K, int BLOCK>
+template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
     using P = Pack<DT, VEC>;
+    constexpr int ES = ElemSize<DT>::value;
     constexpr int RPB = BLOCK / TPR;
     extern __shared__ float lds[];
 
     const int N = a.N;
+    const int64_t M = a.M;
+    const uint32_t row_bytes = (uint32_t)N * ES;
     const int nchunk = N / VEC;
     const int grp = threadIdx.x / TPR;
     const int lt = threadIdx.x % TPR;
-    const bool fused = a.residual != nullptr;
+    const uint32_t goff = (uint32_t)grp * row_bytes;
 
-    float g[K][VEC];
+    uint32_t coff[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int c = lt + k * TPR;
-        P gp = c < nchunk ? load_pack_cached<DT, VEC>(a.gamma, (int64_t)c * VEC) : zero_pack<DT, VEC>();
+        coff[k] = c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
+    }
+    P gp[K];
+    {
+        const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) g[k][e] = elem(gp, e);
+        for (int k = 0; k < K; ++k) gp[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k]);
     }
 
-    P xc[K], rc[K], xn[K], rn[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) xc[k] = rc[k] = xn[k] = rn[k] = zero_pack<DT, VEC>();
+    P xs[DEPTH][K], rs[DEPTH][FUSED ? K : 1];
+    const int64_t wstride = (int64_t)gridDim.x * RPB;
+    const int64_t w0 = (int64_t)blockIdx.x * RPB;
+    // the row's rstd is written by thread 0 of its group
+    const uint32_t rstd_off = lt == 0 ? (uint32_t)grp * 4u : OOB;
 
-    const int64_t M = a.M;
-    const int64_t stride = (int64_t)gridDim.x * RPB;
-    int64_t base = (int64_t)blockIdx.x * RPB;
-
-    auto load_row = [&](int64_t row, P (&xv)[K], P (&rv)[K]) {
-        const int64_t off = row * N;
+    auto load_window = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1]) {
+        const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
+        const rsrc_t rx = make_rsrc(at(a.x, wb * N, ES), bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int c = lt + k * TPR;
-            if (c < nchunk) {
-                xv[k] = load_pack<DT, VEC>(a.x, off + (int64_t)c * VEC);
-                if (fused) rv[k] = load_pack<DT, VEC>(a.residual, off + (int64_t)c * VEC);
-            }
+        for (int k = 0; k < K; ++k) xv[k] = buf_load<DT, VEC, AUX_NT>(rx, goff + coff[k]);
+        if constexpr (FUSED) {
+            const rsrc_t rz = make_rsrc(at(a.residual, wb * N, ES), bytes);
+#pragma unroll
+            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_NT>(rz, goff + coff[k]);
         }
     };
 
-    if (base + grp < M) load_row(base + grp, xc, rc);
-    int parity = 0;
-    for (; base < M; base += stride) {
-        const int64_t row = base + grp;
-        const int64_t nrow = row + stride;
-        if (nrow < M) load_row(nrow, xn, rn);
-        const bool valid = row < M;
-
-        float v[K][VEC];
+    auto process = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1], int parity) {
+        const uint32_t nr = rows_in<RPB>(wb, M);
         float part = 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float t = elem(xc[k], e);
-                if (fused) t = round_trip<DT>(t + elem(rc[k], e));
-                v[k][e] = t;
-                part = fmaf(t, t, part);
-            }
-        const float ms = row_sum<TPR, BLOCK>(part, lds, parity) / (float)N;
-        const float r = 1.0f / sqrtf(ms + a.eps);
-
-        if (valid) {
-            const int64_t off = row * N;
-            if (lt == 0) a.rstd[row] = r;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int c = lt + k * TPR;
-                if (c < nchunk) {
-                    float o[VEC];
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) o[e] = v[k][e] * r * g[k][e];
-                    store_pack<DT, VEC>(a.y, off + (int64_t)c * VEC, make_pack<DT, VEC>(o));
-                    if (fused) store_pack<DT, VEC>(a.residual_out, off + (int64_t)c * VEC,
-                                                   make_pack<DT, VEC>(v[k]));
-                }
-            }
-        }
+        P av[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            xc[k] = xn[k];
-            rc[k] = rn[k];
+            if constexpr (FUSED) {
+                float t[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) t[e] = elem(xv[k], e) + elem(rv[k], e);
+                av[k] = make_pack<DT, VEC>(t);  // added, rounded once to the dtype
+            } else {
+                av[k] = xv[k];
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float v = elem(av[k], e);
+                part = fmaf(v, v, part);
+            }
         }
-        parity ^= 1;
+        const float ms = row_sum<TPR, BLOCK>(part, lds, parity) / (float)N;
+        const float r = 1.0f / sqrtf(ms + a.eps);
+        buf_store_f32(make_rsrc(at(a.rstd, wb, 4), nr * 4u), rstd_off, r);
+        const uint32_t bytes = nr * row_bytes;
+        const rsrc_t ry = make_rsrc(at(a.y, wb * N, ES), bytes);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float o[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = elem(av[k], e) * r * elem(gp[k], e);
+            buf_store<DT, VEC, AUX_NT>(ry, goff + coff[k], make_pack<DT, VEC>(o));
+        }
+        if constexpr (FUSED) {
+            const rsrc_t ro = make_rsrc(at(a.residual_out, wb * N, ES), bytes);
+#pragma unroll
+            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_NT>(ro, goff + coff[k], av[k]);
+        }
+    };
+
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load_window(w0 + s * wstride, xs[s], rs[s]);
+    int parity = 0;
+    int64_t base = w0;
+    for (; base + (DEPTH - 1) * wstride < M; base += DEPTH * wstride) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+            const int64_t wb = base + s * wstride;
+            process(wb, xs[s], rs[s], parity);
+            parity ^= 1;
+            load_window(wb + DEPTH * wstride, xs[s], rs[s]);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s) {
+        const int64_t wb = base + s * wstride;
+        if (wb < M) {
+            process(wb, xs[s], rs[s], parity);
+            parity ^= 1;
+        }
     }
 }
 
@@ -378,15 +434,26 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
 // Launchers
 // ---------------------------------------------------------------------------
 
-template <int TPR> constexpr int block_of() { return TPR > 256 ? TPR : 256; }
+template <int TPR> constexpr int block_of() { return TPR > RMSN_BLOCK_MIN ? TPR : RMSN_BLOCK_MIN; }
+
+// Windows in flight per row group: RMSN_DEPTH where a wave may use up to 256
+// VGPRs; 1024-thread blocks (128 VGPRs a wave) keep two, or one on the
+// element path, whose rows take a register per element.
+template <int VEC, int TPR> constexpr int ring_depth() {
+    return block_of<TPR>() >= 1024 ? (VEC == 1 ? 1 : 2) : RMSN_DEPTH;
+}
 
 template <int DT, int VEC, int TPR, int K>
 static hipError_t launch_bwd_cfg(const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
+    constexpr int D = ring_depth<VEC, TPR>();
     const size_t lds = (size_t)(2 * RPB * WPR + (RPB > 1 ? TPR * K * VEC : 0)) * sizeof(float);
-    hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK>), dim3(grid), dim3(BLOCK), lds, s, a);
+    if (a.dres)
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, D, true>), dim3(grid), dim3(BLOCK), lds, s, a);
+    else
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, D, false>), dim3(grid), dim3(BLOCK), lds, s, a);
     return hipGetLastError();
 }
 
@@ -395,52 +462,72 @@ static hipError_t launch_fwd_cfg(const FwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
+    constexpr int D = ring_depth<VEC, TPR>();
     const size_t lds = (size_t)(2 * RPB * WPR) * sizeof(float);
-    hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK>), dim3(grid), dim3(BLOCK), lds, s, a);
+    if (a.residual)
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, D, true>), dim3(grid), dim3(BLOCK), lds, s, a);
+    else
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, D, false>), dim3(grid), dim3(BLOCK), lds, s, a);
     return hipGetLastError();
 }
 
 // Dispatch a row plan to its kernel instance. Every (vec, tpr, k) that
 // plan_rows can return has an instance here; anything else is a bug and is
 // reported as hipErrorInvalidValue without launching.
-#define RMSN_DISPATCH(LAUNCH, ARGS, GRID, STREAM)                                              \
-    do {                                                                                       \
-        constexpr int VW = 16 / ElemSize<DT>::value;                                           \
-        if (p.vec == VW) {                                                                     \
-            if (p.tpr == 16 && p.k == 1) return LAUNCH<DT, VW, 16, 1>(ARGS, GRID, STREAM);     \
-            if (p.tpr == 16 && p.k == 2) return LAUNCH<DT, VW, 16, 2>(ARGS, GRID, STREAM);     \
-            if (p.k == 4) {                                                                    \
-                switch (p.tpr) {                                                               \
-                case 16: return LAUNCH<DT, VW, 16, 4>(ARGS, GRID, STREAM);                     \
-                case 32: return LAUNCH<DT, VW, 32, 4>(ARGS, GRID, STREAM);                     \
-                case 64: return LAUNCH<DT, VW, 64, 4>(ARGS, GRID, STREAM);                     \
-                case 128: return LAUNCH<DT, VW, 128, 4>(ARGS, GRID, STREAM);                   \
-                case 256: return LAUNCH<DT, VW, 256, 4>(ARGS, GRID, STREAM);                   \
-                case 512: return LAUNCH<DT, VW, 512, 4>(ARGS, GRID, STREAM);                   \
-                case 1024:                                                                     \
-                    if constexpr (VW == 4) return LAUNCH<DT, VW, 1024, 4>(ARGS, GRID, STREAM); \
-                    break;                                                                     \
-                default: break;                                                                \
-                }                                                                              \
-            }                                                                                  \
-        } else if (p.vec == 1) {                                                               \
-            if (p.tpr == 64 && p.k == 4) return LAUNCH<DT, 1, 64, 4>(ARGS, GRID, STREAM);      \
-            if (p.tpr == 64 && p.k == 8) return LAUNCH<DT, 1, 64, 8>(ARGS, GRID, STREAM);      \
-            if (p.tpr == 64 && p.k == 16) return LAUNCH<DT, 1, 64, 16>(ARGS, GRID, STREAM);    \
-            if (p.tpr == 256 && p.k == 16) return LAUNCH<DT, 1, 256, 16>(ARGS, GRID, STREAM);  \
-            if (p.tpr == 1024 && p.k == 16) return LAUNCH<DT, 1, 1024, 16>(ARGS, GRID, STREAM); \
-        }                                                                                      \
-        return hipErrorInvalidValue;                                                           \
-    } while (0)
+// Dispatch of (vec, tpr, k) to a kernel instance. Every plan plan_rows can
+// return has an instance; anything else is reported as hipErrorInvalidValue
+// without a launch.
+template <template <int, int, int, int> class L, int DT, int VW, int K, class A>
+static hipError_t by_tpr(int tpr, const A &a, int grid, hipStream_t s) {
+    switch (tpr) {
+    case 16: return L<DT, VW, 16, K>::go(a, grid, s);
+    case 32: return L<DT, VW, 32, K>::go(a, grid, s);
+    case 64: return L<DT, VW, 64, K>::go(a, grid, s);
+    case 128: return L<DT, VW, 128, K>::go(a, grid, s);
+    case 256: return L<DT, VW, 256, K>::go(a, grid, s);
+    case 512: return L<DT, VW, 512, K>::go(a, grid, s);
+    case 1024: return L<DT, VW, 1024, K>::go(a, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <template <int, int, int, int> class L, int DT, class A>
+static hipError_t dispatch(const RowPlan &p, const A &a, int grid, hipStream_t s) {
+    constexpr int VW = 16 / ElemSize<DT>::value;
+    if (p.vec == VW) {
+        if (p.tpr == 16 && p.k == 1) return L<DT, VW, 16, 1>::go(a, grid, s);
+        if (p.tpr == 16 && p.k == 2) return L<DT, VW, 16, 2>::go(a, grid, s);
+        if (p.k == RMSN_K_TARGET) return by_tpr<L, DT, VW, RMSN_K_TARGET>(p.tpr, a, grid, s);
+        if (p.k == 4) return by_tpr<L, DT, VW, 4>(p.tpr, a, grid, s);
+    } else if (p.vec == 1) {
+        if (p.tpr == 64 && p.k == 4) return L<DT, 1, 64, 4>::go(a, grid, s);
+        if (p.tpr == 64 && p.k == 8) return L<DT, 1, 64, 8>::go(a, grid, s);
+        if (p.tpr == 64 && p.k == 16) return L<DT, 1, 64, 16>::go(a, grid, s);
+        if (p.tpr == 256 && p.k == 16) return L<DT, 1, 256, 16>::go(a, grid, s);
+        if (p.tpr == 1024 && p.k == 16) return L<DT, 1, 1024, 16>::go(a, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DT, int VEC, int TPR, int K> struct BwdLaunch {
+    static hipError_t go(const BwdArgs &a, int grid, hipStream_t s) {
+        return launch_bwd_cfg<DT, VEC, TPR, K>(a, grid, s);
+    }
+};
+template <int DT, int VEC, int TPR, int K> struct FwdLaunch {
+    static hipError_t go(const FwdArgs &a, int grid, hipStream_t s) {
+        return launch_fwd_cfg<DT, VEC, TPR, K>(a, grid, s);
+    }
+};
 
 template <int DT>
 static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s) {
-    RMSN_DISPATCH(launch_bwd_cfg, a, grid, s);
+    return dispatch<BwdLaunch, DT>(p, a, grid, s);
 }
 
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
-    RMSN_DISPATCH(launch_fwd_cfg, a, grid, s);
+    return dispatch<FwdLaunch, DT>(p, a, grid, s);
 }
 
 template <int DT>
@@ -462,8 +549,8 @@ static hipError_t launch_bwd_dt(const RowPlan &p, const BwdArgs &args, int grid,
     if (a.mode == DG_PARTIAL) {
         a.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + WS_HEADER);
         if ((e = dispatch_bwd<DT>(p, a, grid, s)) != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_finalize_kernel<DT>, dim3((a.N + 63) / 64), dim3(256), 0, s, a.partials, grid,
-                           a.N, a.dgamma_f32, a.dgamma);
+        hipLaunchKernelGGL(bwd_finalize_kernel<DT>, dim3((a.N + FIN_COLS - 1) / FIN_COLS),
+                           dim3(FIN_COLS * FIN_SPLIT), 0, s, a.partials, grid, a.N, a.dgamma_f32, a.dgamma);
         return hipGetLastError();
     }
     if (a.mode == DG_ATOMIC) {

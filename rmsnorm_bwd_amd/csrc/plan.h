@@ -28,6 +28,24 @@ inline int pow2_ceil(int64_t v) {
     return p;
 }
 
+// Build-time tuning knobs (defaults measured on MI355X):
+//   RMSN_BWD_MAX_BLOCKS  cap of the backward's persistent grid
+//   RMSN_BLOCK_MIN       threads per block when a row needs fewer
+//   RMSN_K_TARGET        16-byte chunks per thread on the vector path
+//   RMSN_DEPTH           row windows in flight per row group (blocks <= 512)
+#ifndef RMSN_BWD_MAX_BLOCKS
+#define RMSN_BWD_MAX_BLOCKS 256
+#endif
+#ifndef RMSN_BLOCK_MIN
+#define RMSN_BLOCK_MIN 256
+#endif
+#ifndef RMSN_K_TARGET
+#define RMSN_K_TARGET 4
+#endif
+#ifndef RMSN_DEPTH
+#define RMSN_DEPTH 3
+#endif
+
 // Largest supported row length.
 constexpr int64_t MAX_N = 16384;
 
@@ -46,9 +64,12 @@ inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
             p->tpr = 16;
             p->k = C <= 16 ? 1 : (C <= 32 ? 2 : 4);
         } else {
-            // 4 chunks per thread; 1024 threads (fp32 rows above 8192) hold 16 elements
-            p->tpr = pow2_ceil((C + 3) / 4);
-            p->k = 4;
+            p->k = RMSN_K_TARGET;
+            p->tpr = pow2_ceil((C + p->k - 1) / p->k);
+            if (p->tpr > 1024) {  // long fp32 rows: 4 chunks of 1024 threads (16 elements)
+                p->tpr = 1024;
+                p->k = 4;
+            }
         }
     } else {
         p->vec = 1;
@@ -63,14 +84,14 @@ inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
             p->k = 16;
         }
     }
-    p->block = p->tpr > 256 ? p->tpr : 256;
+    p->block = p->tpr > RMSN_BLOCK_MIN ? p->tpr : RMSN_BLOCK_MIN;
     p->rpb = p->block / p->tpr;
     return true;
 }
 
 // Upper bound on the backward's persistent grid: the number of per-block
 // fp32 dgamma partials the workspace must hold.
-constexpr int BWD_MAX_BLOCKS = 256;
+constexpr int BWD_MAX_BLOCKS = RMSN_BWD_MAX_BLOCKS;
 constexpr size_t WS_HEADER = 256;
 
 // Blocks the backward launches for M rows: one block per rpb rows at small M,
