@@ -144,11 +144,22 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE)
     ap.add_argument("--hot", action="store_true", help="time one buffer set only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one device-to-device copy of MIB MiB (a kernel of "
+                         "known traffic, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(dgamma would need one all-reduce per step across GPUs).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = workloads.WORKLOADS[args.workload]
     d = workloads.make_inputs(w)

@@ -97,9 +97,10 @@ int fused_add_rmsnorm_fwd_rstd(const void *x, const void *residual, const void *
                                int64_t M, int64_t N, float eps, int dtype, void *stream);
 
 /* Bytes of device workspace the backward entry points need for (M, N, dtype,
- * flags). The answer never exceeds 256 + 256 * N * 4 bytes. The caller allocates at least this much, 256-byte aligned, and passes it to
- * rmsnorm_bwd / fused_add_rmsnorm_bwd. Returns 0 for arguments the backward
- * would reject. Makes no HIP call. */
+ * flags). The answer never exceeds 256 + 256 * N16 * 4 bytes, N16 being N
+ * rounded up to a multiple of 16. The caller allocates at least this much,
+ * 256-byte aligned, and passes it to rmsnorm_bwd / fused_add_rmsnorm_bwd.
+ * Returns 0 for arguments the backward would reject. Makes no HIP call. */
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags);
 
 /* RMSNorm backward. [I769] Implementation plan, Math; [P800] PR-1 commit:

@@ -81,6 +81,15 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on_device(device, fn, *args):
+    """Call fn with `device` current (the library launches on the current
+    device, as the pages' device guard requires), switching only if needed."""
+    if device.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
+
+
 def _rows(x, gamma, name):
     """(M, N) view of x with the pages' guards: last dim == len(gamma), contiguous."""
     if gamma.dim() != 1:
@@ -121,9 +130,8 @@ def rmsnorm_fwd_rstd(x, gamma, eps, y=None, rstd=None):
     rstd = torch.empty(M, dtype=torch.float32, device=x.device) if rstd is None else rstd
     _same("rmsnorm_fwd_rstd", x, gamma, y)
     _check_rstd(rstd, M, x.device)
-    with torch.cuda.device(x.device):
-        st = lib().rmsnorm_fwd_rstd(_p(x2), _p(gamma), _p(y), _p(rstd), M, N, float(eps), dt,
-                                    _stream(x.device))
+    st = _on_device(x.device, lambda: lib().rmsnorm_fwd_rstd(
+        _p(x2), _p(gamma), _p(y), _p(rstd), M, N, float(eps), dt, _stream(x.device)))
     _raise_on("rmsnorm_fwd_rstd", st)
     return y, rstd
 
@@ -140,10 +148,9 @@ def fused_add_rmsnorm_fwd_rstd(x, residual, gamma, eps, out=None, residual_out=N
     rstd = torch.empty(M, dtype=torch.float32, device=x.device) if rstd is None else rstd
     _same("fused_add_rmsnorm_fwd_rstd", x, residual, gamma, out, residual_out)
     _check_rstd(rstd, M, x.device)
-    with torch.cuda.device(x.device):
-        st = lib().fused_add_rmsnorm_fwd_rstd(_p(x2), _p(residual), _p(gamma), _p(out),
-                                              _p(residual_out), _p(rstd), M, N, float(eps), dt,
-                                              _stream(x.device))
+    st = _on_device(x.device, lambda: lib().fused_add_rmsnorm_fwd_rstd(
+        _p(x2), _p(residual), _p(gamma), _p(out), _p(residual_out), _p(rstd), M, N, float(eps),
+        dt, _stream(x.device)))
     _raise_on("fused_add_rmsnorm_fwd_rstd", st)
     return out, residual_out, rstd
 
@@ -177,16 +184,14 @@ def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags)
     need = rmsnorm_bwd_workspace_bytes(M, N, dt, flags)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
-        if fn == "rmsnorm_bwd":
-            st = lib().rmsnorm_bwd(_p(x2), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32),
-                                   _p(dgamma), _p(workspace), workspace.numel(), M, N, dt,
-                                   int(flags), _stream(x.device))
-        else:
-            st = lib().fused_add_rmsnorm_bwd(_p(x2), _p(gamma), _p(dy), _p(dres), _p(rstd), _p(dx),
-                                             _p(dgamma_f32), _p(dgamma), _p(workspace),
-                                             workspace.numel(), M, N, dt, int(flags),
-                                             _stream(x.device))
+    if fn == "rmsnorm_bwd":
+        st = _on_device(x.device, lambda: lib().rmsnorm_bwd(
+            _p(x2), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma),
+            _p(workspace), workspace.numel(), M, N, dt, int(flags), _stream(x.device)))
+    else:
+        st = _on_device(x.device, lambda: lib().fused_add_rmsnorm_bwd(
+            _p(x2), _p(gamma), _p(dy), _p(dres), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma),
+            _p(workspace), workspace.numel(), M, N, dt, int(flags), _stream(x.device)))
     _raise_on(fn, st)
     return dx, dgamma_f32, dgamma
 

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     // ---- this block's dgamma partial ----
     auto emit = [&](int j, float v) {
         if (a.mode == DG_PARTIAL) {
-            a.partials[(int64_t)blockIdx.x * N + j] = v;
+            a.partials[partial_index(j, blockIdx.x, gridDim.x)] = v;
         } else if (a.mode == DG_ATOMIC) {
             unsafeAtomicAdd(a.dgamma_f32 + j, v);
         } else {
@@ -253,46 +253,46 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Backward, dgamma finalize (deterministic mode): dgamma_f32[j] = sum over the
-// G block partials in a fixed order, and its rounding to the dtype. A block
-// owns 32 adjacent columns (one 128-byte line of each partial row) and 16
-// splits; split w sums partials w, w + 16, ..., issuing all of its loads
-// before the first add, so the kernel waits for memory once. The 16 sums are
-// then added in split order.
+// G block partials in a fixed order, and its rounding to the dtype.
+// The partials are stored in tiles of 16 columns: tile t is a [G][16] block
+// of floats, so the 16 partial rows of a tile are one contiguous run of
+// G * 64 bytes. One 256-thread block reduces one tile: thread i owns column
+// i % 16 and rows i / 16 + 16 k (k = 0, 1, ...), issuing all its loads before
+// the first add (for each k the block reads 1 KiB contiguously), then the 16
+// per-thread sums of a column are added in row order through LDS.
 // ---------------------------------------------------------------------------
-constexpr int FIN_COLS = 32;
-constexpr int FIN_SPLIT = 16;
-constexpr int FIN_LOADS = (BWD_MAX_BLOCKS + FIN_SPLIT - 1) / FIN_SPLIT;
+constexpr int FIN_LOADS = (BWD_MAX_BLOCKS + FIN_TILE - 1) / FIN_TILE;
 
 template <int DT>
-__global__ __launch_bounds__(FIN_COLS *FIN_SPLIT) void bwd_finalize_kernel(const float *__restrict__ partials,
-                                                                          int G, int N,
-                                                                          float *__restrict__ dgamma_f32,
-                                                                          void *__restrict__ dgamma) {
-    __shared__ float red[FIN_SPLIT][FIN_COLS];
-    const int l = threadIdx.x % FIN_COLS;
-    const int split = threadIdx.x / FIN_COLS;
-    const int col = blockIdx.x * FIN_COLS + l;
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(const float *__restrict__ partials, int G, int N,
+                                                           float *__restrict__ dgamma_f32,
+                                                           void *__restrict__ dgamma) {
+    __shared__ float red[FIN_TILE][FIN_TILE];
+    const int c = threadIdx.x % FIN_TILE;
+    const int r0 = threadIdx.x / FIN_TILE;
+    const float *tile = partials + (int64_t)blockIdx.x * G * FIN_TILE;
     float v[FIN_LOADS];
 #pragma unroll
-    for (int i = 0; i < FIN_LOADS; ++i) {
-        const int gi = split + i * FIN_SPLIT;
-        v[i] = (col < N && gi < G) ? partials[(int64_t)gi * N + col] : 0.f;
+    for (int k = 0; k < FIN_LOADS; ++k) {
+        const int g = r0 + FIN_TILE * k;
+        v[k] = g < G ? tile[g * FIN_TILE + c] : 0.f;
     }
-    float s = v[0];
+    float t = v[0];
 #pragma unroll
-    for (int i = 1; i < FIN_LOADS; ++i) s += v[i];
-    red[split][l] = s;
+    for (int k = 1; k < FIN_LOADS; ++k) t += v[k];
+    red[r0][c] = t;
     __syncthreads();
-    if (split == 0 && col < N) {
-        float t = red[0][l];
+    const int col = blockIdx.x * FIN_TILE + c;
+    if (r0 == 0 && col < N) {
+        float sum = red[0][c];
 #pragma unroll
-        for (int w = 1; w < FIN_SPLIT; ++w) t += red[w][l];
-        dgamma_f32[col] = t;
+        for (int w = 1; w < FIN_TILE; ++w) sum += red[w][c];
+        dgamma_f32[col] = sum;
         if (dgamma) {
             if constexpr (DT == DT_F32) {
-                static_cast<float *>(dgamma)[col] = t;
+                static_cast<float *>(dgamma)[col] = sum;
             } else {
-                static_cast<uint16_t *>(dgamma)[col] = pack1<DT>(t);
+                static_cast<uint16_t *>(dgamma)[col] = pack1<DT>(sum);
             }
         }
     }
@@ -549,8 +549,8 @@ static hipError_t launch_bwd_dt(const RowPlan &p, const BwdArgs &args, int grid,
     if (a.mode == DG_PARTIAL) {
         a.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + WS_HEADER);
         if ((e = dispatch_bwd<DT>(p, a, grid, s)) != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_finalize_kernel<DT>, dim3((a.N + FIN_COLS - 1) / FIN_COLS),
-                           dim3(FIN_COLS * FIN_SPLIT), 0, s, a.partials, grid, a.N, a.dgamma_f32, a.dgamma);
+        hipLaunchKernelGGL(bwd_finalize_kernel<DT>, dim3((a.N + FIN_TILE - 1) / FIN_TILE), dim3(256), 0, s,
+                           a.partials, grid, a.N, a.dgamma_f32, a.dgamma);
         return hipGetLastError();
     }
     if (a.mode == DG_ATOMIC) {

@@ -105,11 +105,24 @@ inline int64_t bwd_blocks(int64_t M, const RowPlan &p) {
 // dgamma combining modes actually run.
 enum : int { DG_DIRECT = 0, DG_PARTIAL = 1, DG_ATOMIC = 2 };
 
-// Bytes of workspace for a backward call: a header, then one fp32 partial
-// row of N per block when partials are combined by the fixed-order kernel.
+// Block partials of dgamma are stored in tiles of FIN_TILE columns: tile t
+// holds, for every block g, the block's partials of columns
+// [FIN_TILE t, FIN_TILE (t + 1)) contiguously, so one tile is a [G][FIN_TILE]
+// array and the finalize reads it in one contiguous run.
+constexpr int FIN_TILE = 16;
+
+constexpr int64_t partial_index(int64_t col, int64_t block, int64_t G) {
+    return (col / FIN_TILE) * G * FIN_TILE + block * FIN_TILE + col % FIN_TILE;
+}
+
+// Bytes of workspace for a backward call: a header, then the tiled fp32 block
+// partials when they are combined by the fixed-order kernel.
 inline size_t bwd_workspace(int64_t M, int64_t N, const RowPlan &p, int mode) {
     size_t ws = WS_HEADER;
-    if (mode == DG_PARTIAL) ws += (size_t)bwd_blocks(M, p) * (size_t)N * sizeof(float);
+    if (mode == DG_PARTIAL) {
+        const int64_t tiles = (N + FIN_TILE - 1) / FIN_TILE;
+        ws += (size_t)bwd_blocks(M, p) * (size_t)(tiles * FIN_TILE) * sizeof(float);
+    }
     return ws;
 }
 

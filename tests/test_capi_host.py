@@ -186,4 +186,4 @@ def test_workspace_query():
         for N in (1, 3, 255, 3000, 4096, 16384):
             for dt in (R.F32, R.F16, R.BF16):
                 v = q(M, N, dt)
-                assert 256 <= v <= 256 + 256 * N * 4
+                assert 256 <= v <= 256 + 256 * (-(-N // 16) * 16) * 4
