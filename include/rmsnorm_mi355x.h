@@ -60,8 +60,8 @@ typedef enum {
  *   RMSN_DGAMMA_DETERMINISTIC  partials go to the workspace and a second
  *                              kernel sums them in a fixed order: the same
  *                              inputs give the same bits on every call;
- *   RMSN_DGAMMA_ATOMIC         partials are added with fp32 atomics into the
- *                              workspace; the sum order, so the last bits of
+ *   RMSN_DGAMMA_ATOMIC         partials are added with fp32 atomics into
+ *                              dgamma_f32; the sum order, so the last bits of
  *                              dgamma, may vary from call to call.
  * RMSN_CHECK_DEVICE additionally checks, with the HIP runtime, that every
  * pointer belongs to the current device (the fault the pages' device guard

@@ -160,6 +160,21 @@ def rmsnorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
     return int(lib().rmsnorm_bwd_workspace_bytes(int(M), int(N), code, int(flags)))
 
 
+# One workspace per (device, stream), reused by calls that pass none: calls on
+# one stream run in order, so they never share it concurrently, and a call
+# then allocates nothing.
+_workspaces = {}
+
+
+def _cached_workspace(device, need):
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def _check_rstd(rstd, M, device):
     if rstd.dtype != torch.float32 or rstd.numel() != M or not rstd.is_contiguous() \
             or rstd.device != device:
@@ -183,7 +198,7 @@ def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags)
         raise ValueError(f"{fn}: dgamma must have N elements")
     need = rmsnorm_bwd_workspace_bytes(M, N, dt, flags)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        workspace = _cached_workspace(x.device, need)
     if fn == "rmsnorm_bwd":
         st = _on_device(x.device, lambda: lib().rmsnorm_bwd(
             _p(x2), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma),

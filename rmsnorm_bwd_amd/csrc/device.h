@@ -127,9 +127,15 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int RSRC_WORD3 = 0x00020000;
 // An offset no descriptor range reaches (every range here is below 2^31).
 constexpr uint32_t OOB = 0x80000000u;
-// Cache-policy bits of a buffer access on gfx950: NT marks data streamed once.
+// Cache-policy bits of a buffer access on gfx950 (bit 0 SC0, bit 1 NT,
+// bit 4 SC1): NT marks data streamed once. AUX_STREAM_STORE is the policy of
+// the streamed row stores (dx, y, residual_out), a build-time knob.
 constexpr int AUX_DEFAULT = 0;
 constexpr int AUX_NT = 2;
+#ifndef RMSN_STORE_AUX
+#define RMSN_STORE_AUX 2
+#endif
+constexpr int AUX_STREAM_STORE = RMSN_STORE_AUX;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, RSRC_WORD3);
@@ -191,6 +197,24 @@ __device__ __forceinline__ Pack<DT, VEC> zero_pack() {
 template <int DT, int VEC>
 __device__ __forceinline__ void opaque(Pack<DT, VEC> &a, Pack<DT, VEC> &b) {
     asm volatile("" : "+v"(a.v), "+v"(b.v));
+}
+
+// An empty asm statement that reads the pack's registers: every load still
+// in flight into them must have arrived before this point.
+template <int DT, int VEC>
+__device__ __forceinline__ void consume(const Pack<DT, VEC> &a) {
+    asm volatile("" : : "v"(a.v));
+}
+
+// Ends a window's arithmetic: its packed results exist before this point and
+// no memory access moves across it. Without it the compiler hoists the next
+// window's loads above the last uses of the current window's registers, and
+// the ring slot then needs a register copy at the loop's back edge, which
+// must wait for those loads.
+template <int DT, int VEC, int K>
+__device__ __forceinline__ void settle(const Pack<DT, VEC> (&out)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) asm volatile("" : : "v"(out[k].v) : "memory");
 }
 
 // ---------------------------------------------------------------------------

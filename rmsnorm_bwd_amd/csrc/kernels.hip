@@ -151,8 +151,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
 
     // The same arithmetic as the definition, with the per-row factors pulled
     // out of the per-element work: sum x_hat*wdy = r * sum x*wdy, and
-    // dx = (wdy - x_hat*c1) * r = r*wdy - (r*r*c1)*x.
-    auto process = [&](int64_t wb, P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, int parity) {
+    // dx = (wdy - x_hat*c1) * r = r*wdy - (r*r*c1)*x. The window's dx is packed
+    // into `out`; the caller issues the next window's loads before the stores
+    // (see the loop below).
+    auto compute = [&](P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, int parity, P (&out)[K]) {
         float part = 0.f;
 #pragma unroll
         for (int k = 0; k < K; ++k)
@@ -164,8 +166,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         // fp32 values live across the sum.
 #pragma unroll
         for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
-
-        const rsrc_t rw = make_rsrc(at(a.dx, wb * N, ES), rows_in<RPB>(wb, M) * row_bytes);
+        // The same for rstd. Passing its ring register through an in-place
+        // asm also keeps the register allocator from moving the slot's next
+        // rstd into a different register, which would need a copy, and a
+        // wait for that load, at the loop's back edge.
+        float r2 = r;
+        asm volatile("" : "+v"(r2));
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             float o[VEC];
@@ -173,44 +179,78 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             for (int e = 0; e < VEC; ++e) {
                 const float xv_e = elem(xv[k], e);
                 const float dyv = elem(dv[k], e);
-                float d = fmaf(-b, xv_e, r * (dyv * elem(gp[k], e)));
+                float d = fmaf(-b, xv_e, r2 * (dyv * elem(gp[k], e)));
                 if constexpr (FUSED) d += elem(rv[k], e);
                 o[e] = d;
-                acc[k][e] = fmaf(dyv, xv_e * r, acc[k][e]);
+                acc[k][e] = fmaf(dyv, xv_e * r2, acc[k][e]);
             }
-            buf_store<DT, VEC, AUX_NT>(rw, goff + coff[k], make_pack<DT, VEC>(o));
+            out[k] = make_pack<DT, VEC>(o);
         }
     };
+    auto store_dx = [&](int64_t wb, const P (&out)[K]) {
+        const rsrc_t rw = make_rsrc(at(a.dx, wb * N, ES), rows_in<RPB>(wb, M) * row_bytes);
+#pragma unroll
+        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(rw, goff + coff[k], out[k]);
+    };
 
+    // Block b takes the windows b, b + G, b + 2G, ... (G blocks in the grid).
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s]);
     int parity = 0;
-    // Steady state: groups of DEPTH windows that all hold rows, with no branch
-    // in the body, so every wait counts exactly the loads it needs.
+    // Steady state: groups of DEPTH windows that all hold rows, with no
+    // branch in the body, so every wait counts exactly the loads it
+    // needs. Loads and stores retire through one in-order counter, so
+    // each window's stores are issued after the loads that refill its
+    // ring slot: waiting for a load then never means waiting for a store
+    // issued after it (in particular, the loads of windows past the last
+    // row, issued in the final group, never hold up the end of the kernel
+    // behind the last stores).
     int64_t base = w0;
     for (; base + (DEPTH - 1) * wstride < M; base += DEPTH * wstride) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
             const int64_t wb = base + s * wstride;
-            process(wb, xs[s], ds[s], rs[s], rr[s], parity);
+            P out[K];
+            compute(xs[s], ds[s], rs[s], rr[s], parity, out);
             parity ^= 1;
+            settle(out);
             load_window(wb + DEPTH * wstride, xs[s], ds[s], rs[s], rr[s]);
+            store_dx(wb, out);
         }
     }
-    // The last, partial group (block-uniform test): its rows are already loaded.
+    // Take delivery of every load still in flight into the ring, in one
+    // wait that only covers stores issued at least a window earlier.
+    // After it no load is pending, so the branches of the last, partial
+    // group cannot make a later wait conservative (with one in-order
+    // counter for loads and stores, a conservative wait would also wait
+    // for every store).
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            consume(xs[s][k]);
+            consume(ds[s][k]);
+            if constexpr (FUSED) consume(rs[s][k]);
+        }
+    // The last, partial group (block-uniform test): its rows are loaded.
 #pragma unroll
     for (int s = 0; s < DEPTH - 1; ++s) {
         const int64_t wb = base + s * wstride;
         if (wb < M) {
-            process(wb, xs[s], ds[s], rs[s], rr[s], parity);
+            P out[K];
+            compute(xs[s], ds[s], rs[s], rr[s], parity, out);
             parity ^= 1;
+            store_dx(wb, out);
         }
     }
 
     // ---- this block's dgamma partial ----
-    auto emit = [&](int j, float v) {
+    // Partials go to the workspace in 16-byte stores, marked streaming so
+    // they do not sit dirty in L2 when the kernel ends: the finalize reads
+    // them back from memory in any case.
+    auto emit1 = [&](int j, float v) {
         if (a.mode == DG_PARTIAL) {
-            a.partials[partial_index(j, blockIdx.x, gridDim.x)] = v;
+            __builtin_nontemporal_store(v, a.partials + partial_index(j, blockIdx.x, gridDim.x));
         } else if (a.mode == DG_ATOMIC) {
             unsafeAtomicAdd(a.dgamma_f32 + j, v);
         } else {
@@ -224,13 +264,35 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             }
         }
     };
+    // four consecutive columns j..j+3 (j a multiple of 4, all < N) lie in one
+    // partial tile, so one 16-byte store writes them
+    auto emit4 = [&](int j, float v0, float v1, float v2, float v3) {
+        if (a.mode == DG_PARTIAL) {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            f32x4 v = {v0, v1, v2, v3};
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<f32x4 *>(a.partials + partial_index(j, blockIdx.x, gridDim.x)));
+        } else {
+            emit1(j, v0);
+            emit1(j + 1, v1);
+            emit1(j + 2, v2);
+            emit1(j + 3, v3);
+        }
+    };
     if constexpr (RPB == 1) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = lt + k * TPR;
-            if (c < nchunk)
+            if (c < nchunk) {
+                if constexpr (VEC % 4 == 0) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) emit(c * VEC + e, acc[k][e]);
+                    for (int e = 0; e < VEC; e += 4)
+                        emit4(c * VEC + e, acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) emit1(c * VEC + e, acc[k][e]);
+                }
+            }
         }
     } else {
         // fold the rpb row groups in a fixed order, then write the block's row
@@ -247,7 +309,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             }
             __syncthreads();
         }
-        for (int j = threadIdx.x; j < N; j += BLOCK) emit(j, comb[j]);
+        const int n4 = N & ~3;
+        for (int j = threadIdx.x * 4; j < n4; j += BLOCK * 4) emit4(j, comb[j], comb[j + 1], comb[j + 2], comb[j + 3]);
+        for (int j = n4 + threadIdx.x; j < N; j += BLOCK) emit1(j, comb[j]);
     }
 }
 
@@ -368,10 +432,12 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         }
     };
 
-    auto process = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1], int parity) {
+    // Computes the window's outputs (y packed into `yo`, added into `av`)
+    // and stores rstd; y and residual_out are stored by the caller after it
+    // has issued the loads that refill the ring slot.
+    auto compute = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1], int parity, P (&av)[K], P (&yo)[K]) {
         const uint32_t nr = rows_in<RPB>(wb, M);
         float part = 0.f;
-        P av[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if constexpr (FUSED) {
@@ -391,41 +457,59 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         const float ms = row_sum<TPR, BLOCK>(part, lds, parity) / (float)N;
         const float r = 1.0f / sqrtf(ms + a.eps);
         buf_store_f32(make_rsrc(at(a.rstd, wb, 4), nr * 4u), rstd_off, r);
-        const uint32_t bytes = nr * row_bytes;
-        const rsrc_t ry = make_rsrc(at(a.y, wb * N, ES), bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             float o[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[e] = elem(av[k], e) * r * elem(gp[k], e);
-            buf_store<DT, VEC, AUX_NT>(ry, goff + coff[k], make_pack<DT, VEC>(o));
+            yo[k] = make_pack<DT, VEC>(o);
         }
+    };
+    auto store_rows = [&](int64_t wb, const P (&av)[K], const P (&yo)[K]) {
+        const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
+        const rsrc_t ry = make_rsrc(at(a.y, wb * N, ES), bytes);
+#pragma unroll
+        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ry, goff + coff[k], yo[k]);
         if constexpr (FUSED) {
             const rsrc_t ro = make_rsrc(at(a.residual_out, wb * N, ES), bytes);
 #pragma unroll
-            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_NT>(ro, goff + coff[k], av[k]);
+            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ro, goff + coff[k], av[k]);
         }
     };
 
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) load_window(w0 + s * wstride, xs[s], rs[s]);
     int parity = 0;
+    // As in the backward: full groups without branches, and each window's
+    // stores issued after the loads that refill its ring slot.
     int64_t base = w0;
     for (; base + (DEPTH - 1) * wstride < M; base += DEPTH * wstride) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
             const int64_t wb = base + s * wstride;
-            process(wb, xs[s], rs[s], parity);
+            P av[K], yo[K];
+            compute(wb, xs[s], rs[s], parity, av, yo);
             parity ^= 1;
+            settle(yo);
             load_window(wb + DEPTH * wstride, xs[s], rs[s]);
+            store_rows(wb, av, yo);
         }
     }
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            consume(xs[s][k]);
+            if constexpr (FUSED) consume(rs[s][k]);
+        }
 #pragma unroll
     for (int s = 0; s < DEPTH - 1; ++s) {
         const int64_t wb = base + s * wstride;
         if (wb < M) {
-            process(wb, xs[s], rs[s], parity);
+            P av[K], yo[K];
+            compute(wb, xs[s], rs[s], parity, av, yo);
             parity ^= 1;
+            store_rows(wb, av, yo);
         }
     }
 }
@@ -434,13 +518,18 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
 // Launchers
 // ---------------------------------------------------------------------------
 
-template <int TPR> constexpr int block_of() { return TPR > RMSN_BLOCK_MIN ? TPR : RMSN_BLOCK_MIN; }
+template <int TPR> constexpr int block_of() { return block_threads(TPR); }
 
-// Windows in flight per row group: RMSN_DEPTH where a wave may use up to 256
-// VGPRs; 1024-thread blocks (128 VGPRs a wave) keep two, or one on the
-// element path, whose rows take a register per element.
-template <int VEC, int TPR> constexpr int ring_depth() {
-    return block_of<TPR>() >= 1024 ? (VEC == 1 ? 1 : 2) : RMSN_DEPTH;
+// Windows in flight per row group, sized so the ring fits the registers a wave
+// may use without spilling: blocks of up to 512 threads give a wave 256
+// VGPRs, which hold RMSN_DEPTH windows while a thread's share of one row array
+// takes under 16 registers, two windows under 32 (one with the fused
+// variant's third array) and one beyond.
+template <int VEC, int TPR, int K, bool FUSED> constexpr int ring_depth() {
+    static_assert(block_of<TPR>() <= 512, "blocks of at most 512 threads");
+    constexpr int regs = VEC == 1 ? K : 4 * K;  // registers of one row array's share
+    if (regs >= 32 || (regs >= 16 && FUSED && VEC > 1)) return 1;
+    return regs >= 16 && RMSN_DEPTH > 2 ? 2 : RMSN_DEPTH;
 }
 
 template <int DT, int VEC, int TPR, int K>
@@ -448,12 +537,13 @@ static hipError_t launch_bwd_cfg(const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
-    constexpr int D = ring_depth<VEC, TPR>();
+    constexpr int DF = ring_depth<VEC, TPR, K, true>();
+    constexpr int DP = ring_depth<VEC, TPR, K, false>();
     const size_t lds = (size_t)(2 * RPB * WPR + (RPB > 1 ? TPR * K * VEC : 0)) * sizeof(float);
     if (a.dres)
-        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, D, true>), dim3(grid), dim3(BLOCK), lds, s, a);
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DF, true>), dim3(grid), dim3(BLOCK), lds, s, a);
     else
-        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, D, false>), dim3(grid), dim3(BLOCK), lds, s, a);
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DP, false>), dim3(grid), dim3(BLOCK), lds, s, a);
     return hipGetLastError();
 }
 
@@ -462,18 +552,16 @@ static hipError_t launch_fwd_cfg(const FwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
-    constexpr int D = ring_depth<VEC, TPR>();
+    constexpr int DF = ring_depth<VEC, TPR, K, true>();
+    constexpr int DP = ring_depth<VEC, TPR, K, false>();
     const size_t lds = (size_t)(2 * RPB * WPR) * sizeof(float);
     if (a.residual)
-        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, D, true>), dim3(grid), dim3(BLOCK), lds, s, a);
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DF, true>), dim3(grid), dim3(BLOCK), lds, s, a);
     else
-        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, D, false>), dim3(grid), dim3(BLOCK), lds, s, a);
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DP, false>), dim3(grid), dim3(BLOCK), lds, s, a);
     return hipGetLastError();
 }
 
-// Dispatch a row plan to its kernel instance. Every (vec, tpr, k) that
-// plan_rows can return has an instance here; anything else is a bug and is
-// reported as hipErrorInvalidValue without launching.
 // Dispatch of (vec, tpr, k) to a kernel instance. Every plan plan_rows can
 // return has an instance; anything else is reported as hipErrorInvalidValue
 // without a launch.
@@ -486,7 +574,6 @@ static hipError_t by_tpr(int tpr, const A &a, int grid, hipStream_t s) {
     case 128: return L<DT, VW, 128, K>::go(a, grid, s);
     case 256: return L<DT, VW, 256, K>::go(a, grid, s);
     case 512: return L<DT, VW, 512, K>::go(a, grid, s);
-    case 1024: return L<DT, VW, 1024, K>::go(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -494,17 +581,31 @@ static hipError_t by_tpr(int tpr, const A &a, int grid, hipStream_t s) {
 template <template <int, int, int, int> class L, int DT, class A>
 static hipError_t dispatch(const RowPlan &p, const A &a, int grid, hipStream_t s) {
     constexpr int VW = 16 / ElemSize<DT>::value;
+    static_assert(RMSN_TPR_MAX == 512 || RMSN_TPR_MAX == 256, "row thread cap");
     if (p.vec == VW) {
-        if (p.tpr == 16 && p.k == 1) return L<DT, VW, 16, 1>::go(a, grid, s);
-        if (p.tpr == 16 && p.k == 2) return L<DT, VW, 16, 2>::go(a, grid, s);
-        if (p.k == RMSN_K_TARGET) return by_tpr<L, DT, VW, RMSN_K_TARGET>(p.tpr, a, grid, s);
-        if (p.k == 4) return by_tpr<L, DT, VW, 4>(p.tpr, a, grid, s);
+        if (p.tpr == 16) {  // short rows inside one wavefront
+            if (p.k == 1) return L<DT, VW, 16, 1>::go(a, grid, s);
+            if (p.k == 2) return L<DT, VW, 16, 2>::go(a, grid, s);
+            if (p.k == 4) return L<DT, VW, 16, 4>::go(a, grid, s);
+        }
+        if (p.k == RMSN_K_MIN && p.tpr < RMSN_TPR_MAX) return by_tpr<L, DT, VW, RMSN_K_MIN>(p.tpr, a, grid, s);
+        if (p.tpr == RMSN_TPR_MAX) {
+            switch (p.k) {
+            case 1: return L<DT, VW, RMSN_TPR_MAX, 1>::go(a, grid, s);
+            case 2: return L<DT, VW, RMSN_TPR_MAX, 2>::go(a, grid, s);
+            case 4: return L<DT, VW, RMSN_TPR_MAX, 4>::go(a, grid, s);
+            case 8:  // only fp32 rows are long enough
+                if constexpr (VW == 4) return L<DT, VW, RMSN_TPR_MAX, 8>::go(a, grid, s);
+                break;
+            default: break;
+            }
+        }
     } else if (p.vec == 1) {
         if (p.tpr == 64 && p.k == 4) return L<DT, 1, 64, 4>::go(a, grid, s);
         if (p.tpr == 64 && p.k == 8) return L<DT, 1, 64, 8>::go(a, grid, s);
         if (p.tpr == 64 && p.k == 16) return L<DT, 1, 64, 16>::go(a, grid, s);
         if (p.tpr == 256 && p.k == 16) return L<DT, 1, 256, 16>::go(a, grid, s);
-        if (p.tpr == 1024 && p.k == 16) return L<DT, 1, 1024, 16>::go(a, grid, s);
+        if (p.tpr == 512 && p.k == 32) return L<DT, 1, 512, 32>::go(a, grid, s);
     }
     return hipErrorInvalidValue;
 }

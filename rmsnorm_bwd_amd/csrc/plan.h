@@ -9,7 +9,7 @@
 namespace rmsn {
 
 // How one row is spread over threads. A "row group" of tpr threads (a power of
-// two, 16..1024) owns one row at a time; thread t of the group owns the vector
+// two, 16..512) owns one row at a time; thread t of the group owns the vector
 // chunks t, t + tpr, ..., t + (k - 1) * tpr, each vec elements wide. A block of
 // `block` threads holds rpb = block / tpr row groups. Rows of up to 64 threads
 // live inside one wavefront (several short rows per wavefront when tpr < 64);
@@ -30,21 +30,38 @@ inline int pow2_ceil(int64_t v) {
 
 // Build-time tuning knobs (defaults measured on MI355X):
 //   RMSN_BWD_MAX_BLOCKS  cap of the backward's persistent grid
-//   RMSN_BLOCK_MIN       threads per block when a row needs fewer
-//   RMSN_K_TARGET        16-byte chunks per thread on the vector path
+//   RMSN_BLOCK_MIN       threads per block when a row spans 2..4 wavefronts
+//   RMSN_BLOCK_WAVE      threads per block when a row fits in one wavefront
+//   RMSN_TPR_MAX         most threads one row is spread over on the vector path
+//   RMSN_K_MIN           fewest 16-byte chunks per thread on the vector path
 //   RMSN_DEPTH           row windows in flight per row group (blocks <= 512)
 #ifndef RMSN_BWD_MAX_BLOCKS
 #define RMSN_BWD_MAX_BLOCKS 256
 #endif
 #ifndef RMSN_BLOCK_MIN
-#define RMSN_BLOCK_MIN 256
+#define RMSN_BLOCK_MIN 512
 #endif
-#ifndef RMSN_K_TARGET
-#define RMSN_K_TARGET 4
+#ifndef RMSN_BLOCK_WAVE
+#define RMSN_BLOCK_WAVE 256
+#endif
+#ifndef RMSN_TPR_MAX
+#define RMSN_TPR_MAX 512
+#endif
+#ifndef RMSN_K_MIN
+#define RMSN_K_MIN 1
 #endif
 #ifndef RMSN_DEPTH
 #define RMSN_DEPTH 3
 #endif
+
+// Threads per block for rows of tpr threads. Rows inside one wavefront
+// (several per wavefront when tpr < 64) run in 256-thread blocks: larger
+// blocks would leave each block too few row windows for its load ring to
+// hide latency. Wider rows run in blocks of 512 threads, or of tpr when it
+// is larger.
+constexpr int block_threads(int tpr) {
+    return tpr <= 64 ? RMSN_BLOCK_WAVE : (tpr > RMSN_BLOCK_MIN ? tpr : RMSN_BLOCK_MIN);
+}
 
 // Largest supported row length.
 constexpr int64_t MAX_N = 16384;
@@ -52,8 +69,10 @@ constexpr int64_t MAX_N = 16384;
 // Choose the row plan for N elements of esize bytes. vector_ok says every
 // row-tensor pointer and gamma are 16-byte aligned; the vector path also needs
 // N to be a multiple of the vector width so that every row start stays aligned.
-// A thread holds at most 32 elements of a row (16 in 1024-thread blocks,
-// whose waves get at most 128 VGPRs). Returns false when N is out of range.
+// Longer rows take more chunks per thread rather than more threads: a row
+// spreads over at most 512 threads, so a thread holds up to 32 elements of a
+// 16384-element row, and every block has at most 512 threads (whose waves
+// may use 256 VGPRs). Returns false when N is out of range.
 inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
     if (N < 1 || N > MAX_N) return false;
     const int vw = 16 / esize;
@@ -64,12 +83,12 @@ inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
             p->tpr = 16;
             p->k = C <= 16 ? 1 : (C <= 32 ? 2 : 4);
         } else {
-            p->k = RMSN_K_TARGET;
-            p->tpr = pow2_ceil((C + p->k - 1) / p->k);
-            if (p->tpr > 1024) {  // long fp32 rows: 4 chunks of 1024 threads (16 elements)
-                p->tpr = 1024;
-                p->k = 4;
-            }
+            // the fewest chunks (a power of two, at least RMSN_K_MIN) that fit
+            // the row in RMSN_TPR_MAX threads
+            int k = RMSN_K_MIN;
+            while ((int64_t)k * RMSN_TPR_MAX < C) k <<= 1;
+            p->k = k;
+            p->tpr = pow2_ceil((C + k - 1) / k);
         }
     } else {
         p->vec = 1;
@@ -80,11 +99,11 @@ inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
             p->tpr = 256;
             p->k = 16;
         } else {
-            p->tpr = 1024;
-            p->k = 16;
+            p->tpr = 512;
+            p->k = 32;
         }
     }
-    p->block = p->tpr > RMSN_BLOCK_MIN ? p->tpr : RMSN_BLOCK_MIN;
+    p->block = block_threads(p->tpr);
     p->rpb = p->block / p->tpr;
     return true;
 }
