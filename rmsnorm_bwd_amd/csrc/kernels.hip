@@ -137,13 +137,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         const rsrc_t rd = make_rsrc(at(a.dy, wb * N, ES), bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            xv[k] = buf_load<DT, VEC, AUX_NT>(rx, goff + coff[k]);
-            dv[k] = buf_load<DT, VEC, AUX_NT>(rd, goff + coff[k]);
+            xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, goff + coff[k]);
+            dv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, goff + coff[k]);
         }
         if constexpr (FUSED) {
             const rsrc_t rz = make_rsrc(at(a.dres, wb * N, ES), bytes);
 #pragma unroll
-            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_NT>(rz, goff + coff[k]);
+            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, goff + coff[k]);
         }
         const rsrc_t rt = make_rsrc(at(a.rstd, wb, 4), rows_in<RPB>(wb, M) * 4u);
         r = buf_load_f32(rt, (uint32_t)grp * 4u);
@@ -190,7 +190,8 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     auto store_dx = [&](int64_t wb, const P (&out)[K]) {
         const rsrc_t rw = make_rsrc(at(a.dx, wb * N, ES), rows_in<RPB>(wb, M) * row_bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(rw, goff + coff[k], out[k]);
+        for (int k = 0; k < K; ++k)
+            buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_DX_STORE>(rw, goff + coff[k], out[k]);
     };
 
     // Block b takes the windows b, b + G, b + 2G, ... (G blocks in the grid).
@@ -424,11 +425,11 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
         const rsrc_t rx = make_rsrc(at(a.x, wb * N, ES), bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) xv[k] = buf_load<DT, VEC, AUX_NT>(rx, goff + coff[k]);
+        for (int k = 0; k < K; ++k) xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, goff + coff[k]);
         if constexpr (FUSED) {
             const rsrc_t rz = make_rsrc(at(a.residual, wb * N, ES), bytes);
 #pragma unroll
-            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_NT>(rz, goff + coff[k]);
+            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, goff + coff[k]);
         }
     };
 
