@@ -63,6 +63,22 @@ __device__ __forceinline__ const void *at(const void *base, int64_t elem, int es
     return reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(base) + (uintptr_t)(elem * es));
 }
 
+// Store of a dgamma partial: plain (the default), so that the partials stay
+// in the caches for the finalize that reads them right after, or
+// non-temporal with RMSN_PARTIAL_NT. Measured on MI355X: plain stores take
+// 4096 x 4096 bf16 from 22.05 to 20.9 us.
+#ifndef RMSN_PARTIAL_NT
+#define RMSN_PARTIAL_NT 0
+#endif
+template <class V>
+__device__ __forceinline__ void partial_store(V v, V *p) {
+#if RMSN_PARTIAL_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
 // Rows of the window starting at row wb that exist: min(RPB, M - wb), >= 0.
 template <int RPB>
 __device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
@@ -195,8 +211,16 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     };
 
     // Block b takes the windows b, b + G, b + 2G, ... (G blocks in the grid).
+    // The first windows' loads, in window order: the fence keeps the
+    // scheduler from sinking a window's rstd load below later windows' row
+    // loads, which would make the memory counter's sequence on entering the
+    // loop differ from the one on its back edge; the compiler then merges
+    // the two pessimistically and waits for windows a step does not use.
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s]);
+    for (int s = 0; s < DEPTH; ++s) {
+        load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s]);
+        asm volatile("" ::: "memory");
+    }
     int parity = 0;
     // Steady state: groups of DEPTH windows that all hold rows, with no
     // branch in the body, so every wait counts exactly the loads it
@@ -246,12 +270,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     }
 
     // ---- this block's dgamma partial ----
-    // Partials go to the workspace in 16-byte stores, marked streaming so
-    // they do not sit dirty in L2 when the kernel ends: the finalize reads
-    // them back from memory in any case.
+    // Partials go to the workspace in 16-byte stores where the columns allow.
     auto emit1 = [&](int j, float v) {
         if (a.mode == DG_PARTIAL) {
-            __builtin_nontemporal_store(v, a.partials + partial_index(j, blockIdx.x, gridDim.x));
+            partial_store(v, a.partials + partial_index(j, blockIdx.x, gridDim.x));
         } else if (a.mode == DG_ATOMIC) {
             unsafeAtomicAdd(a.dgamma_f32 + j, v);
         } else {
@@ -271,8 +293,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         if (a.mode == DG_PARTIAL) {
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             f32x4 v = {v0, v1, v2, v3};
-            __builtin_nontemporal_store(
-                v, reinterpret_cast<f32x4 *>(a.partials + partial_index(j, blockIdx.x, gridDim.x)));
+            partial_store(v, reinterpret_cast<f32x4 *>(a.partials + partial_index(j, blockIdx.x, gridDim.x)));
         } else {
             emit1(j, v0);
             emit1(j + 1, v1);
@@ -479,7 +500,10 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
     };
 
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load_window(w0 + s * wstride, xs[s], rs[s]);
+    for (int s = 0; s < DEPTH; ++s) {
+        load_window(w0 + s * wstride, xs[s], rs[s]);
+        asm volatile("" ::: "memory");  // window order, as in the backward
+    }
     int parity = 0;
     // As in the backward: full groups without branches, and each window's
     // stores issued after the loads that refill its ring slot.
@@ -521,16 +545,18 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
 
 template <int TPR> constexpr int block_of() { return block_threads(TPR); }
 
-// Windows in flight per row group, sized so the ring fits the registers a wave
-// may use without spilling: blocks of up to 512 threads give a wave 256
-// VGPRs, which hold RMSN_DEPTH windows while a thread's share of one row array
-// takes under 16 registers, two windows under 32 (one with the fused
-// variant's third array) and one beyond.
+// Windows in flight per row group: as many as fit RMSN_RING_VGPRS registers
+// of ring, at most RMSN_DEPTH and at least one. A window costs, per row array
+// (2, or 3 for the fused variant), 8 registers per 16-byte chunk on the vector
+// path and 2 per element on the element path (the loaded bytes plus the
+// unpacked values the arithmetic keeps live). With blocks of up to 512 threads a
+// wave may use 256 VGPRs; the budget leaves room for gamma, the dgamma
+// accumulators and the arithmetic, so that no instance spills.
 template <int VEC, int TPR, int K, bool FUSED> constexpr int ring_depth() {
     static_assert(block_of<TPR>() <= 512, "blocks of at most 512 threads");
-    constexpr int regs = VEC == 1 ? K : 4 * K;  // registers of one row array's share
-    if (regs >= 32 || (regs >= 16 && FUSED && VEC > 1)) return 1;
-    return regs >= 16 && RMSN_DEPTH > 2 ? 2 : RMSN_DEPTH;
+    constexpr int per_window = (FUSED ? 3 : 2) * (VEC == 1 ? 2 * K : 8 * K);
+    constexpr int d = RMSN_RING_VGPRS / per_window;
+    return d < 1 ? 1 : (d > RMSN_DEPTH ? RMSN_DEPTH : d);
 }
 
 template <int DT, int VEC, int TPR, int K>

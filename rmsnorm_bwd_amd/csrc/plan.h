@@ -34,7 +34,8 @@ inline int pow2_ceil(int64_t v) {
 //   RMSN_BLOCK_WAVE      threads per block when a row fits in one wavefront
 //   RMSN_TPR_MAX         most threads one row is spread over on the vector path
 //   RMSN_K_MIN           fewest 16-byte chunks per thread on the vector path
-//   RMSN_DEPTH           row windows in flight per row group (blocks <= 512)
+//   RMSN_DEPTH           most row windows in flight per row group
+//   RMSN_RING_VGPRS      registers per thread the window ring may take
 #ifndef RMSN_BWD_MAX_BLOCKS
 #define RMSN_BWD_MAX_BLOCKS 256
 #endif
@@ -52,6 +53,9 @@ inline int pow2_ceil(int64_t v) {
 #endif
 #ifndef RMSN_DEPTH
 #define RMSN_DEPTH 3
+#endif
+#ifndef RMSN_RING_VGPRS
+#define RMSN_RING_VGPRS 144
 #endif
 
 // Threads per block for rows of tpr threads. Rows inside one wavefront
