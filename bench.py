@@ -94,6 +94,56 @@ def time_calls(fn, sets, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def copy_bandwidth(mib=512, reps=10):
+    """Achievable HBM bandwidth on this part: a device-to-device copy of
+    `mib` MiB (twice the memory-side cache), read + write bytes per second."""
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms = time_calls(lambda _: dst.copy_(src), [None], reps, 2)
+    del src, dst
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
+def _graph_us(fn, calls=20, replays=50):
+    """GPU time per call of fn, captured `calls` times in one HIP graph and
+    replayed: the host's launch overhead is out of the measurement."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    ms = time_calls(lambda _: graph.replay(), [None], replays, 3)
+    return ms * 1e3 / calls
+
+
+def latency_floor(w_name="plain_1x4096_bf16"):
+    """The one-row backward (a single kernel), per call, against a
+    one-element torch kernel, both replayed from a HIP graph so that only GPU
+    time counts; the graph's dx is checked against an eager call's."""
+    w = workloads.WORKLOADS[w_name]
+    d = workloads.make_inputs(w)
+    g, sets = make_sets(w, d, 1)
+    s = sets[0]
+    call_bwd(w, g, s)
+    torch.cuda.synchronize()
+    eager = s["dx"].clone()
+    s["dx"].zero_()
+    us = _graph_us(lambda: call_bwd(w, g, s))
+    torch.cuda.synchronize()
+    t = torch.zeros(1, device="cuda:0")
+    us_empty = _graph_us(lambda: t.add_(1.0))
+    return {"workload": w_name, "us_per_call": round(us, 2), "one_element_kernel_us": round(us_empty, 2),
+            "timing": "HIP graph replay", "graph_matches_eager": bool(torch.equal(eager, s["dx"]))}
+
+
 def cpu_baseline(w, d, calls=5):
     """The CPU oracle (fp64, single thread) on the same workload."""
     import oracle
@@ -180,6 +230,10 @@ def main():
 
     abytes = algorithmic_bytes(w)
     gbps = abytes / (ms * 1e-3) / 1e9
+    # the copy and the one-row case are skipped under the counter runs, whose
+    # only copy must be the calibration copy
+    copy_gbps = None if args.copy_calibration else copy_bandwidth()
+    latency = None if args.copy_calibration else latency_floor()
     line = {
         "metric": "rmsnorm_bwd us/call + achieved HBM GB/s (% of peak), 4096x4096 bf16",
         "value": round(ms * 1e3, 2),
@@ -199,6 +253,9 @@ def main():
         "achieved_GBps": round(gbps, 1),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "hot_cache_us": round(ms_hot * 1e3, 2),
+        "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
+        "pct_of_copy": round(100 * gbps / copy_gbps, 1) if copy_gbps else None,
+        "latency": latency,
         "fwd_rstd_us": round(ms_fwd * 1e3, 2),
         "fwd_rstd_GBps": round(fwd_bytes(w) / (ms_fwd * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,

@@ -223,3 +223,7 @@ def fused_add_rmsnorm_bwd(added, gamma, dy, dresidual_out, rstd, dx=None, dgamma
     dx is also the gradient of the residual."""
     return _bwd("fused_add_rmsnorm_bwd", added, gamma, dy, dresidual_out, rstd, dx, dgamma_f32,
                 dgamma, workspace, flags)
+
+
+from .autograd import (FusedAddRMSNormFunction, RMSNormFunction, fused_add_rmsnorm,  # noqa: E402,F401
+                       rmsnorm)

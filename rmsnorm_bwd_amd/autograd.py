@@ -1,0 +1,93 @@
+"""Autograd wrappers over the C ABI binding.
+
+``rmsnorm(x, weight, eps)`` and ``fused_add_rmsnorm(x, residual, weight, eps,
+prenorm=True)`` are differentiable: their forward runs the library's forward
+that saves rstd, their backward runs the library's backward. Like the rest
+of the package they only marshal arguments; every step runs in the HIP
+kernels.
+
+Pages cited, by title:
+  [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
+         rstd) to enable training / downstream (quack) integration" - Scope /
+         tasks, item 3: an autograd Function whose forward saves x, weight
+         and rstd and whose backward calls the backward kernel; item 4: the
+         gradient with respect to residual_out for the fused-add path.
+  [P800] FlyDSL PR #800, "[rmsnorm] Add fused-add / residual backward (PR
+         2/3, #769)" - PR-1 commit: RMSNormFunction and a public
+         rmsnorm(x, weight, eps) over inputs of any rank (rows are the last
+         dimension); fused-add commit and PR body: FusedAddRMSNormFunction,
+         whose prenorm form returns (out, residual_out) and whose backward
+         takes the gradient of residual_out as well; the gradient of x is
+         also the gradient of residual, returned as the same tensor.
+"""
+import torch
+
+from . import fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, rmsnorm_bwd, rmsnorm_fwd_rstd
+
+
+def _weight_grad(dgamma_f32, dgamma, weight):
+    """dgamma in the weight's dtype: the fp32 sum itself for fp32 weights,
+    else the library's round-to-nearest-even copy."""
+    return dgamma_f32 if weight.dtype == torch.float32 else dgamma
+
+
+class RMSNormFunction(torch.autograd.Function):
+    """y = x * rstd * weight over the last dimension, rstd = 1/sqrt(mean(x^2) + eps)."""
+
+    @staticmethod
+    def forward(ctx, x, weight, eps):
+        x = x.contiguous()
+        weight = weight.contiguous()
+        y, rstd = rmsnorm_fwd_rstd(x, weight, eps)
+        ctx.save_for_backward(x, weight, rstd)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, weight, rstd = ctx.saved_tensors
+        dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
+        dx, dgamma_f32, dgamma = rmsnorm_bwd(x, weight, dy.contiguous(), rstd, dgamma=dgamma)
+        return dx, _weight_grad(dgamma_f32, dgamma, weight), None
+
+
+class FusedAddRMSNormFunction(torch.autograd.Function):
+    """residual_out = x + residual (one rounding), out = rmsnorm(residual_out)."""
+
+    @staticmethod
+    def forward(ctx, x, residual, weight, eps):
+        x = x.contiguous()
+        residual = residual.contiguous()
+        weight = weight.contiguous()
+        out, residual_out, rstd = fused_add_rmsnorm_fwd_rstd(x, residual, weight, eps)
+        ctx.save_for_backward(residual_out, weight, rstd)
+        return out, residual_out
+
+    @staticmethod
+    def backward(ctx, dout, dresidual_out):
+        added, weight, rstd = ctx.saved_tensors
+        if dout is None:
+            dout = torch.zeros_like(added)
+        dres = None if dresidual_out is None else dresidual_out.contiguous()
+        dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
+        dx, dgamma_f32, dgamma = fused_add_rmsnorm_bwd(added, weight, dout.contiguous(), dres, rstd,
+                                                       dgamma=dgamma)
+        # x and residual enter only through their sum: one gradient for both
+        return dx, dx, _weight_grad(dgamma_f32, dgamma, weight), None
+
+
+def rmsnorm(x, weight, eps=1e-6):
+    """Differentiable RMSNorm over the last dimension of x (any rank)."""
+    if x.shape[-1] != weight.numel():
+        raise ValueError(f"rmsnorm: x.shape[-1]={x.shape[-1]} != weight length {weight.numel()}")
+    return RMSNormFunction.apply(x, weight, eps)
+
+
+def fused_add_rmsnorm(x, residual, weight, eps=1e-6, prenorm=True):
+    """Differentiable fused add + RMSNorm. With prenorm, returns
+    (out, residual_out); otherwise out alone."""
+    if x.shape != residual.shape:
+        raise ValueError("fused_add_rmsnorm: residual must have x's shape")
+    if x.shape[-1] != weight.numel():
+        raise ValueError(f"fused_add_rmsnorm: x.shape[-1]={x.shape[-1]} != weight length {weight.numel()}")
+    out, residual_out = FusedAddRMSNormFunction.apply(x, residual, weight, eps)
+    return (out, residual_out) if prenorm else out
