@@ -1,5 +1,6 @@
 """CPU oracle for RMSNorm forward (saving rstd), backward, and the fused-add
-(prenorm residual) variants: a ctypes wrapper over ``oracle/oracle.c``.
+(prenorm residual) variants, and for LayerNorm (forward saving mean and rstd,
+backward with dbias): a ctypes wrapper over ``oracle/oracle.c``.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package. The GPU library and
@@ -42,10 +43,13 @@ def lib():
         L.orc_fused_add_rmsnorm_fwd.argtypes = [P, P, P, I, I64, I64, D, P, P, P]
         L.orc_rmsnorm_bwd.argtypes = [P, P, P, P, I, I64, I64, P, P]
         L.orc_fused_add_rmsnorm_bwd.argtypes = [P, P, P, P, P, I, I64, I64, P, P]
+        L.orc_layernorm_fwd.argtypes = [P, P, P, I, I64, I64, D, P, P, P]
+        L.orc_layernorm_bwd.argtypes = [P, P, P, P, P, I, I64, I64, P, P, P]
         L.orc_elem_bytes.argtypes = [I]
         for name in ("orc_decode", "orc_encode", "orc_encode_bits", "orc_rmsnorm_fwd",
                      "orc_fused_add_rmsnorm_fwd", "orc_rmsnorm_bwd",
-                     "orc_fused_add_rmsnorm_bwd", "orc_elem_bytes"):
+                     "orc_fused_add_rmsnorm_bwd", "orc_layernorm_fwd", "orc_layernorm_bwd",
+                     "orc_elem_bytes"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -171,3 +175,40 @@ def fused_add_rmsnorm_bwd(added, gamma, dy, dresidual_out, rstd, want_dx=True,
                                            _ptr(dresidual_out), _ptr(rstd), _code(added),
                                            M, N, _ptr(dx), _ptr(dg)), "fused_add_rmsnorm_bwd")
     return dx, dg
+
+
+def layernorm_fwd(x, gamma, beta, eps, want_y=True):
+    """LayerNorm forward that saves its statistics: returns (mean float32
+    (M,), rstd float32 (M,), y float64 (M, N) or None). beta may be None.
+
+    [I769] PR sequence and status updates: the forward saves mean and rstd.
+    """
+    M, N = _shape(x, gamma)
+    if beta is not None and (beta.shape != gamma.shape or beta.dtype != gamma.dtype):
+        raise ValueError("oracle: beta must match gamma")
+    mean = torch.empty(M, dtype=torch.float32)
+    rstd = torch.empty(M, dtype=torch.float32)
+    y = torch.empty((M, N), dtype=torch.float64) if want_y else None
+    _check(lib().orc_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _code(x), M, N,
+                                   float(eps), _ptr(mean), _ptr(rstd), _ptr(y)), "layernorm_fwd")
+    return mean, rstd, y
+
+
+def layernorm_bwd(x, gamma, dy, mean, rstd, want_dx=True, want_dgamma=True, want_dbeta=True):
+    """LayerNorm backward: returns (dx float64 (M, N), dgamma float64 (N,),
+    dbeta float64 (N,)), each None when not wanted.
+
+    [I769] PR sequence: the RMSNorm approach plus mean handling and dbias.
+    """
+    M, N = _shape(x, gamma)
+    for t in (mean, rstd):
+        if t.shape != (M,) or t.dtype != torch.float32:
+            raise ValueError("oracle: mean and rstd must be float32 (M,)")
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("oracle: dy must match x")
+    dx = torch.empty((M, N), dtype=torch.float64) if want_dx else None
+    dg = torch.empty(N, dtype=torch.float64) if want_dgamma else None
+    db = torch.empty(N, dtype=torch.float64) if want_dbeta else None
+    _check(lib().orc_layernorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(mean), _ptr(rstd),
+                                   _code(x), M, N, _ptr(dx), _ptr(dg), _ptr(db)), "layernorm_bwd")
+    return dx, dg, db

@@ -1,7 +1,8 @@
 /*
  * oracle.c - plain, slow, obviously-correct CPU reference for RMSNorm with a
  * saved per-row rstd, its backward, and the fused-add (prenorm residual)
- * variants of both.
+ * variants of both; and for LayerNorm with saved mean and rstd and its
+ * backward with the bias gradient.
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load or call this file. The GPU library never links
@@ -29,12 +30,18 @@
  *     array the GPU path reads), widened exactly to fp64.
  *   - c1 divides by N (a mean over the row).
  *   - a NULL dresidual_out stands for a tensor of zeros.
+ *   - LayerNorm is the textbook one: biased variance (divisor N), eps inside
+ *     the square root, y = x_hat * gamma + beta; a NULL beta is zeros; the
+ *     backward reads the fp32 mean and rstd a forward saved.
  *
  * Parity pins (tests marked "not gpu"): central finite differences of the
  * forward, an explicit O(N^2) Jacobian, float64 torch.autograd on the CPU,
  * closed forms (N = 1, constant rows, dy = 0, M = 1), the orthogonality
  * identity sum_j x_hat_j dx_j = N c1 eps r^3, scale and linearity
  * invariants, and the encode/decode routines against torch's conversions.
+ * LayerNorm: hand-derived worked examples, float64 torch layer_norm
+ * autograd, finite differences, the shift invariance sum_j dx_j = 0, and the
+ * reduction to the RMSNorm backward on zero-mean rows.
  */
 #include <math.h>
 #include <stdint.h>
@@ -326,6 +333,90 @@ int orc_fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *
         if (d_added && dresidual_out)
             for (int64_t j = 0; j < N; ++j)
                 d_added[j] += up(dresidual_out, dtype, i * N + j);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* LayerNorm: forward that saves mean and rstd, backward with dbias.         */
+/* ------------------------------------------------------------------------ */
+
+/* [I769] PR sequence and status updates: the LayerNorm follow-up mirrors the
+ * RMSNorm backward with mean handling and a bias gradient, and its forward
+ * saves mean and rstd (fp32). Taken here as the textbook layer norm over the
+ * N columns of a row: mean = (1/N) sum x, var = (1/N) sum (x - mean)^2
+ * (the biased variance), rstd = 1/sqrt(var + eps),
+ * y = (x - mean) * rstd * gamma + beta. Outputs: mean, rstd (M fp32,
+ * required), y (M*N fp64 unrounded, nullable). beta may be NULL (zeros). */
+int orc_layernorm_fwd(const void *x, const void *gamma, const void *beta, int dtype,
+                      int64_t M, int64_t N, double eps, float *mean, float *rstd, double *y)
+{
+    if (check_common(gamma, dtype, M, N, eps) || (M && (!x || !mean || !rstd)))
+        return ORC_EINVAL;
+    for (int64_t i = 0; i < M; ++i) {
+        double mu = 0.0, var = 0.0, r;
+        for (int64_t j = 0; j < N; ++j)
+            mu += up(x, dtype, i * N + j);
+        mu /= (double)N;
+        for (int64_t j = 0; j < N; ++j) {
+            double d = up(x, dtype, i * N + j) - mu;
+            var += d * d;
+        }
+        var /= (double)N;
+        r = 1.0 / sqrt(var + eps);
+        mean[i] = (float)mu;
+        rstd[i] = (float)r;
+        if (y)
+            for (int64_t j = 0; j < N; ++j) {
+                double v = (up(x, dtype, i * N + j) - mu) * r * up(gamma, dtype, j);
+                y[i * N + j] = beta ? v + up(beta, dtype, j) : v;
+            }
+    }
+    return ORC_OK;
+}
+
+/* The LayerNorm backward, from the definition above, with the fp32 mean and
+ * rstd a forward saved (widened exactly). Per row, with
+ * x_hat = (x - mean) * rstd and wdy = dy * gamma:
+ *   c1 = (1/N) sum x_hat * wdy, c2 = (1/N) sum wdy,
+ *   dx = (wdy - x_hat * c1 - c2) * rstd,
+ * and over all rows dgamma = sum dy * x_hat, dbeta = sum dy.
+ * Outputs (each nullable): dx (M*N fp64 unrounded), dgamma, dbeta (N fp64,
+ * overwritten; zero when M = 0). */
+int orc_layernorm_bwd(const void *x, const void *gamma, const void *dy, const float *mean,
+                      const float *rstd, int dtype, int64_t M, int64_t N, double *dx,
+                      double *dgamma, double *dbeta)
+{
+    if (check_common(gamma, dtype, M, N, 0.0) || (M && (!x || !dy || !mean || !rstd)))
+        return ORC_EINVAL;
+    for (int64_t j = 0; j < N; ++j) {
+        if (dgamma)
+            dgamma[j] = 0.0;
+        if (dbeta)
+            dbeta[j] = 0.0;
+    }
+    for (int64_t i = 0; i < M; ++i) {
+        double mu = (double)mean[i], r = (double)rstd[i];
+        double c1 = 0.0, c2 = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double x_hat = (up(x, dtype, i * N + j) - mu) * r;
+            double wdy = up(dy, dtype, i * N + j) * up(gamma, dtype, j);
+            c1 += x_hat * wdy;
+            c2 += wdy;
+        }
+        c1 /= (double)N;
+        c2 /= (double)N;
+        for (int64_t j = 0; j < N; ++j) {
+            double x_hat = (up(x, dtype, i * N + j) - mu) * r;
+            double dyj = up(dy, dtype, i * N + j);
+            double wdy = dyj * up(gamma, dtype, j);
+            if (dx)
+                dx[i * N + j] = (wdy - x_hat * c1 - c2) * r;
+            if (dgamma)
+                dgamma[j] += dyj * x_hat;
+            if (dbeta)
+                dbeta[j] += dyj;
+        }
     }
     return ORC_OK;
 }

@@ -3,8 +3,9 @@ in tests/test_oracle_pins.py catch every one of them.
 
 Each mutant is a one-line edit of oracle/oracle.c (a dropped term, a flipped
 sign, a wrong index or divisor, a swapped operand), compiled on the CPU into a
-temporary library; the pin suite is run against it in a child process and
-must fail. The oracle source in the repository is never modified.
+temporary library; the pin suite of the function it breaks (RMSNorm or
+LayerNorm) is run against it in a child process and must fail. The oracle
+source in the repository is never modified.
 """
 import os
 import subprocess
@@ -43,6 +44,36 @@ MUTANTS = {
     "rstd_stored_as_sqrt_ms": ("rstd[row] = (float)r;", "rstd[row] = (float)(1.0 / r);"),
 }
 
+# LayerNorm mutants, caught by tests/test_oracle_ln_pins.py
+LN_MUTANTS = {
+    "ln_var_divisor_n_minus_1": ("var /= (double)N;", "var /= (double)(N > 1 ? N - 1 : 1);"),
+    "ln_var_without_mean": ("double d = up(x, dtype, i * N + j) - mu;", "double d = up(x, dtype, i * N + j);"),
+    "ln_eps_outside_sqrt": ("r = 1.0 / sqrt(var + eps);", "r = 1.0 / (sqrt(var) + eps);"),
+    "ln_mean_not_divided": ("mu /= (double)N;", ""),
+    "ln_beta_dropped": ("y[i * N + j] = beta ? v + up(beta, dtype, j) : v;", "y[i * N + j] = v;"),
+    "ln_forward_gamma_dropped": ("double v = (up(x, dtype, i * N + j) - mu) * r * up(gamma, dtype, j);",
+                                 "double v = (up(x, dtype, i * N + j) - mu) * r;"),
+    "ln_mean_saved_unscaled": ("mean[i] = (float)mu;", "mean[i] = (float)(mu * (double)N);"),
+    "ln_c2_dropped": ("dx[i * N + j] = (wdy - x_hat * c1 - c2) * r;", "dx[i * N + j] = (wdy - x_hat * c1) * r;"),
+    "ln_c2_sign_flipped": ("dx[i * N + j] = (wdy - x_hat * c1 - c2) * r;", "dx[i * N + j] = (wdy - x_hat * c1 + c2) * r;"),
+    "ln_c1_sign_flipped": ("dx[i * N + j] = (wdy - x_hat * c1 - c2) * r;", "dx[i * N + j] = (wdy + x_hat * c1 - c2) * r;"),
+    "ln_c2_not_divided": ("c2 /= (double)N;", ""),
+    "ln_c1_not_divided": ("c1 /= (double)N;\n        c2 /= (double)N;", "c2 /= (double)N;"),
+    "ln_dx_rstd_dropped": ("dx[i * N + j] = (wdy - x_hat * c1 - c2) * r;", "dx[i * N + j] = wdy - x_hat * c1 - c2;"),
+    "ln_bwd_x_hat_without_mean": ("double x_hat = (up(x, dtype, i * N + j) - mu) * r;\n            double wdy = up(dy",
+                                  "double x_hat = up(x, dtype, i * N + j) * r;\n            double wdy = up(dy"),
+    "ln_c2_misses_gamma": ("double wdy = up(dy, dtype, i * N + j) * up(gamma, dtype, j);\n            c1 += x_hat * wdy;\n            c2 += wdy;",
+                           "double wdy = up(dy, dtype, i * N + j) * up(gamma, dtype, j);\n            c1 += x_hat * wdy;\n            c2 += up(dy, dtype, i * N + j);"),
+    "ln_dgamma_uses_wdy": ("dgamma[j] += dyj * x_hat;\n            if (dbeta)", "dgamma[j] += wdy * x_hat;\n            if (dbeta)"),
+    "ln_dbeta_uses_wdy": ("dbeta[j] += dyj;", "dbeta[j] += wdy;"),
+    "ln_gamma_wrong_index": ("double wdy = up(dy, dtype, i * N + j) * up(gamma, dtype, j);\n            c1 +=",
+                             "double wdy = up(dy, dtype, i * N + j) * up(gamma, dtype, (j + 1) % N);\n            c1 +="),
+}
+
+PINS = {name: "test_oracle_pins.py" for name in MUTANTS}
+PINS.update({name: "test_oracle_ln_pins.py" for name in LN_MUTANTS})
+MUTANTS.update(LN_MUTANTS)
+
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -56,6 +87,6 @@ def test_pins_catch_mutant(name, tmp_path):
     obuild.build(out=lib, src=str(msrc), extra_flags=["-Wno-error"])
     env = dict(os.environ, ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", PINS[name])],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
