@@ -19,15 +19,16 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = {
     "eps_dropped": ("sumsq / (double)N + eps", "sumsq / (double)N"),
-    "rstd_not_inverted": ("r = 1.0 / sqrt(", "r = sqrt("),
-    "forward_gamma_dropped": ("* r * up(gamma, dtype, j);", "* r;"),
-    "c1_divisor_n_minus_1": ("c1 /= (double)N;", "c1 /= (double)(N > 1 ? N - 1 : 1);"),
-    "c1_not_divided": ("c1 /= (double)N;", ""),
+    "rstd_not_inverted": ("r = 1.0 / sqrt(sumsq", "r = sqrt(sumsq"),
+    "forward_gamma_dropped": ("y[row * N + j] = up(a, dtype, row * N + j) * r * up(gamma, dtype, j);",
+                              "y[row * N + j] = up(a, dtype, row * N + j) * r;"),
+    "c1_divisor_n_minus_1": ("\n    c1 /= (double)N;", "\n    c1 /= (double)(N > 1 ? N - 1 : 1);"),
+    "c1_not_divided": ("\n    c1 /= (double)N;", "\n"),
     "dx_sign_flipped": ("dx_row[j] = (wdy - x_hat * c1) * r;", "dx_row[j] = (wdy + x_hat * c1) * r;"),
     "dx_c1_term_dropped": ("dx_row[j] = (wdy - x_hat * c1) * r;", "dx_row[j] = wdy * r;"),
     "dx_final_rstd_dropped": ("dx_row[j] = (wdy - x_hat * c1) * r;", "dx_row[j] = wdy - x_hat * c1;"),
-    "dgamma_uses_wdy": ("dgamma[j] += dyj * x_hat;", "dgamma[j] += wdy * x_hat;"),
-    "dgamma_uses_x": ("dgamma[j] += dyj * x_hat;", "dgamma[j] += dyj * up(x, dtype, row * N + j);"),
+    "dgamma_uses_wdy": ("dgamma[j] += dyj * x_hat;\n    }", "dgamma[j] += wdy * x_hat;\n    }"),
+    "dgamma_uses_x": ("dgamma[j] += dyj * x_hat;\n    }", "dgamma[j] += dyj * up(x, dtype, row * N + j);\n    }"),
     "gamma_wrong_index": ("double wdy = up(dy, dtype, row * N + j) * up(gamma, dtype, j);",
                           "double wdy = up(dy, dtype, row * N + j) * up(gamma, dtype, (j + row) % N);"),
     "x_hat_reads_dy": ("double x_hat = up(x, dtype, row * N + j) * r;\n        double wdy",
