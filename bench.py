@@ -33,15 +33,20 @@ ROTATE_BYTES = 600 << 20  # > 2 x the 256 MiB memory-side cache
 
 def algorithmic_bytes(w):
     """Bytes the backward must move: read x (or added), dy, [dresidual_out],
-    gamma, rstd; write dx, dgamma_f32 and the dtype copy of dgamma."""
+    gamma, rstd [and mean]; write dx, dgamma_f32 [and dbeta_f32] and their
+    dtype copies."""
     s = w.elem_bytes
     rows = (4 if w.op == "fused" else 3) * w.M * w.N * s
-    return rows + w.N * s + 4 * w.M + 4 * w.N + (w.N * s if s != 4 else 0)
+    ngrad = 2 if w.op == "layernorm" else 1
+    stats = (8 if w.op == "layernorm" else 4) * w.M
+    return rows + w.N * s + stats + ngrad * (4 * w.N + (w.N * s if s != 4 else 0))
 
 
 def fwd_bytes(w):
     s = w.elem_bytes
     rows = (4 if w.op == "fused" else 2) * w.M * w.N * s
+    if w.op == "layernorm":
+        return rows + 2 * w.N * s + 8 * w.M
     return rows + w.N * s + 4 * w.M
 
 
@@ -55,6 +60,13 @@ def make_sets(w, d, nsets):
             x = d["x"].to(dev)
             y, rstd = R.rmsnorm_fwd_rstd(x, g, w.eps)
             s = dict(x=x, dy=d["dy"].to(dev), dres=None, rstd=rstd)
+        elif w.op == "layernorm":
+            x = d["x"].to(dev)
+            beta = d["beta"].to(dev)
+            y, mean, rstd = R.layernorm_fwd_stats(x, g, beta, w.eps)
+            s = dict(x=x, dy=d["dy"].to(dev), dres=None, rstd=rstd, mean=mean, beta=beta,
+                     db32=torch.empty(w.N, dtype=torch.float32, device=dev),
+                     db=torch.empty(w.N, dtype=w.torch_dtype, device=dev))
         else:
             x, res = d["x"].to(dev), d["residual"].to(dev)
             out, added, rstd = R.fused_add_rmsnorm_fwd_rstd(x, res, g, w.eps)
@@ -63,8 +75,8 @@ def make_sets(w, d, nsets):
         s["dx"] = torch.empty_like(s["x"])
         s["dg32"] = torch.empty(w.N, dtype=torch.float32, device=dev)
         s["dg"] = torch.empty(w.N, dtype=w.torch_dtype, device=dev)
-        s["ws"] = torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(w.M, w.N, w.torch_dtype)),
-                              dtype=torch.uint8, device=dev)
+        query = R.layernorm_bwd_workspace_bytes if w.op == "layernorm" else R.rmsnorm_bwd_workspace_bytes
+        s["ws"] = torch.empty(max(256, query(w.M, w.N, w.torch_dtype)), dtype=torch.uint8, device=dev)
         sets.append(s)
     return g, sets
 
@@ -73,6 +85,9 @@ def call_bwd(w, g, s):
     if w.op == "plain":
         R.rmsnorm_bwd(s["x"], g, s["dy"], s["rstd"], dx=s["dx"], dgamma_f32=s["dg32"],
                       dgamma=s["dg"], workspace=s["ws"])
+    elif w.op == "layernorm":
+        R.layernorm_bwd(s["x"], g, s["dy"], s["mean"], s["rstd"], dx=s["dx"], dgamma_f32=s["dg32"],
+                        dbeta_f32=s["db32"], dgamma=s["dg"], dbeta=s["db"], workspace=s["ws"])
     else:
         R.fused_add_rmsnorm_bwd(s["x"], g, s["dy"], s["dres"], s["rstd"], dx=s["dx"],
                                 dgamma_f32=s["dg32"], dgamma=s["dg"], workspace=s["ws"])
@@ -147,10 +162,13 @@ def latency_floor(w_name="plain_1x4096_bf16"):
 def cpu_baseline(w, d, calls=5):
     """The CPU oracle (fp64, single thread) on the same workload."""
     import oracle
-    x = d["x"] if w.op == "plain" else None
+    x = d["x"] if w.op in ("plain", "layernorm") else None
     if w.op == "plain":
         rstd, _ = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps, want_y=False)
         run = lambda: oracle.rmsnorm_bwd(x, d["gamma"], d["dy"], rstd)  # noqa: E731
+    elif w.op == "layernorm":
+        mean, rstd, _ = oracle.layernorm_fwd(d["x"], d["gamma"], d["beta"], w.eps, want_y=False)
+        run = lambda: oracle.layernorm_bwd(d["x"], d["gamma"], d["dy"], mean, rstd)  # noqa: E731
     else:
         added, rstd, _ = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps,
                                                       want_out=False)
@@ -194,6 +212,8 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE)
     ap.add_argument("--hot", action="store_true", help="time one buffer set only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the copy-bandwidth and one-row latency figures (profiled runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device-to-device copy of MIB MiB (a kernel of "
                          "known traffic, to scale hardware byte counters)")
@@ -223,6 +243,8 @@ def main():
     def fwd(s):
         if w.op == "plain":
             R.rmsnorm_fwd_rstd(s["x"], g, w.eps, y=s["dx"], rstd=s["rstd"])
+        elif w.op == "layernorm":
+            R.layernorm_fwd_stats(s["x"], g, s["beta"], w.eps, y=s["dx"], mean=s["mean"], rstd=s["rstd"])
         else:
             R.fused_add_rmsnorm_fwd_rstd(s["x"], s["dy"], g, w.eps, out=s["dx"],
                                          residual_out=s["dres"], rstd=s["rstd"])
@@ -232,10 +254,12 @@ def main():
     gbps = abytes / (ms * 1e-3) / 1e9
     # the copy and the one-row case are skipped under the counter runs, whose
     # only copy must be the calibration copy
-    copy_gbps = None if args.copy_calibration else copy_bandwidth()
-    latency = None if args.copy_calibration else latency_floor()
+    skip = args.copy_calibration or args.no_extras
+    copy_gbps = None if skip else copy_bandwidth()
+    latency = None if skip else latency_floor()
     line = {
-        "metric": "rmsnorm_bwd us/call + achieved HBM GB/s (% of peak), 4096x4096 bf16",
+        "metric": "rmsnorm_bwd us/call + achieved HBM GB/s (% of peak), 4096x4096 bf16"
+                  if w.op != "layernorm" else f"layernorm_bwd us/call + achieved HBM GB/s, {w.name}",
         "value": round(ms * 1e3, 2),
         "unit": "us/call",
         "n_gpus": 1,
@@ -261,7 +285,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic(w),
-                     "kernel": "one rmsnorm_bwd call (main pass + dgamma finalize)",
+                     "kernel": f"one {'layernorm' if w.op == 'layernorm' else 'rmsnorm'}_bwd call "
+                               "(main pass + weight-gradient finalize)",
                      "algorithmic_bytes": abytes},
     }
     if not args.no_cpu:

@@ -1,7 +1,8 @@
 /*
  * rmsnorm_mi355x.h - C ABI of the MI355X (gfx950) RMSNorm library: the
  * forward passes that save a per-row rstd, and the backward passes (dx and the
- * weight gradient dgamma), plain and fused-add (prenorm residual).
+ * weight gradient dgamma), plain and fused-add (prenorm residual); and the
+ * LayerNorm forward (saving mean and rstd) and backward (dx, dgamma, dbeta).
  *
  * Pages cited, by title:
  *   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
@@ -14,9 +15,10 @@
  *     HIP device. The caller owns every buffer, the workspace included. The
  *     library allocates nothing, frees nothing and never synchronises.
  *   - Row tensors are (M, N), row-major and contiguous (row stride N
- *     elements); gamma and the dgamma outputs have N elements; rstd has M.
- *   - One element dtype (rmsn_dtype_t) covers every row tensor and gamma.
- *     rstd and dgamma_f32 are always float32.
+ *     elements); gamma, beta and the weight-gradient outputs have N
+ *     elements; rstd and mean have M.
+ *   - One element dtype (rmsn_dtype_t) covers every row tensor, gamma and
+ *     beta. rstd, mean, dgamma_f32 and dbeta_f32 are always float32.
  *   - Pointers need only element alignment. Rows whose start is not 16-byte
  *     aligned, or N that is not a multiple of the 16-byte vector, take a
  *     slower element-wise path with identical results.
@@ -136,6 +138,38 @@ int fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *dy,
                           int64_t M, int64_t N, int dtype, unsigned flags, void *stream);
 
 /* A static, human-readable name for a status code. */
+/* LayerNorm forward that saves its statistics. [I769] PR sequence and status
+ * updates: the LayerNorm follow-up's forward saves mean and rstd (fp32), with
+ * weight and bias length checks. Taken as the textbook layer norm:
+ *   mean[i] = (1/N) sum_j x[i,j]                         (fp32, stored)
+ *   rstd[i] = 1/sqrt((1/N) sum_j (x[i,j] - mean[i])^2 + eps)   (fp32, stored)
+ *   y[i,j]  = (x[i,j] - mean[i]) * rstd[i] * gamma[j] + beta[j]   (rounded once)
+ * In: x (M,N); gamma (N); beta (N) or NULL for zeros. Out: y (M,N), mean (M),
+ * rstd (M). Errors as rmsnorm_fwd_rstd. */
+int layernorm_fwd_stats(const void *x, const void *gamma, const void *beta, void *y, float *mean,
+                        float *rstd, int64_t M, int64_t N, float eps, int dtype, void *stream);
+
+/* Bytes of workspace layernorm_bwd needs: as rmsnorm_bwd_workspace_bytes with
+ * a second array of partials (dbeta); never more than 256 + 2 * 256 * N16 * 4.
+ * Returns 0 for arguments the backward would reject. Makes no HIP call. */
+size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags);
+
+/* LayerNorm backward. [I769] PR sequence and status updates: the RMSNorm
+ * backward's approach plus mean handling and the bias gradient. Per row,
+ * with x_hat = (x - mean) * rstd and wdy = dy * gamma (fp32),
+ *   c1 = (1/N) sum_j x_hat[j] * wdy[j],  c2 = (1/N) sum_j wdy[j]
+ *   dx[i,j] = (wdy[j] - x_hat[j] * c1 - c2) * rstd[i]    (rounded once)
+ *   dgamma_f32[j] = sum_i dy[i,j] * x_hat[i,j],  dbeta_f32[j] = sum_i dy[i,j]
+ *   dgamma, dbeta = the fp32 sums rounded to the dtype (each nullable)
+ * In: x, dy (M,N); gamma (N); mean, rstd (M, fp32, as saved by
+ * layernorm_fwd_stats). Out: dx (M,N); dgamma_f32 and dbeta_f32 (N fp32,
+ * overwritten); dgamma, dbeta (N, dtype, nullable). Workspace, flags, modes
+ * and errors as rmsnorm_bwd (the modes govern both sums). */
+int layernorm_bwd(const void *x, const void *gamma, const void *dy, const float *mean, const float *rstd,
+                  void *dx, float *dgamma_f32, float *dbeta_f32, void *dgamma, void *dbeta,
+                  void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
+                  unsigned flags, void *stream);
+
 const char *rmsn_status_string(int status);
 
 #ifdef __cplusplus

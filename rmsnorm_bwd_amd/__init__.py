@@ -9,7 +9,10 @@ but every call raises.
 
 Pages cited, by title:
   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
-         rstd) to enable training / downstream (quack) integration"
+         rstd) to enable training / downstream (quack) integration" - also its
+         PR sequence and status updates for the LayerNorm entry points
+         (forward saving mean and rstd, backward with dbias, weight and bias
+         length checks)
   [P800] FlyDSL PR #800, "[rmsnorm] Add fused-add / residual backward
          (PR 2/3, #769)" - its review-fix commit asks for the shape and
          contiguity checks, its fused-add commit for one dtype across operands.
@@ -55,10 +58,14 @@ def lib():
         L.rmsnorm_bwd_workspace_bytes.restype = SZ
         L.rmsnorm_bwd.argtypes = [P, P, P, P, P, P, P, P, SZ, I64, I64, I, U, P]
         L.fused_add_rmsnorm_bwd.argtypes = [P, P, P, P, P, P, P, P, P, SZ, I64, I64, I, U, P]
+        L.layernorm_fwd_stats.argtypes = [P, P, P, P, P, P, I64, I64, F, I, P]
+        L.layernorm_bwd_workspace_bytes.argtypes = [I64, I64, I, U]
+        L.layernorm_bwd_workspace_bytes.restype = SZ
+        L.layernorm_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I, U, P]
         L.rmsn_status_string.argtypes = [I]
         L.rmsn_status_string.restype = ctypes.c_char_p
         for fn in ("rmsnorm_fwd_rstd", "fused_add_rmsnorm_fwd_rstd", "rmsnorm_bwd",
-                   "fused_add_rmsnorm_bwd"):
+                   "fused_add_rmsnorm_bwd", "layernorm_fwd_stats", "layernorm_bwd"):
             getattr(L, fn).restype = I
         _lib = L
     return _lib
@@ -225,5 +232,63 @@ def fused_add_rmsnorm_bwd(added, gamma, dy, dresidual_out, rstd, dx=None, dgamma
                 dgamma, workspace, flags)
 
 
-from .autograd import (FusedAddRMSNormFunction, RMSNormFunction, fused_add_rmsnorm,  # noqa: E402,F401
-                       rmsnorm)
+def layernorm_fwd_stats(x, gamma, beta, eps, y=None, mean=None, rstd=None):
+    """LayerNorm forward that saves mean and rstd. beta may be None (zeros).
+    Returns (y, mean, rstd)."""
+    fn = "layernorm_fwd_stats"
+    dt = _code(x, fn)
+    x2 = _rows(x, gamma, fn)
+    M, N = x2.shape
+    if beta is not None and (beta.dim() != 1 or beta.numel() != N):
+        raise ValueError(f"{fn}: beta must have N={N} elements")
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty(M, dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty(M, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _same(fn, x, gamma, beta, y)
+    _check_rstd(mean, M, x.device)
+    _check_rstd(rstd, M, x.device)
+    st = _on_device(x.device, lambda: lib().layernorm_fwd_stats(
+        _p(x2), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd), M, N, float(eps), dt, _stream(x.device)))
+    _raise_on(fn, st)
+    return y, mean, rstd
+
+
+def layernorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().layernorm_bwd_workspace_bytes(int(M), int(N), code, int(flags)))
+
+
+def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=None, dgamma=None,
+                  dbeta=None, workspace=None, flags=DGAMMA_AUTO):
+    """LayerNorm backward. Returns (dx, dgamma_f32, dbeta_f32, dgamma, dbeta)."""
+    fn = "layernorm_bwd"
+    dt = _code(x, fn)
+    x2 = _rows(x, gamma, fn)
+    M, N = x2.shape
+    if dy.shape != x.shape:
+        raise ValueError(f"{fn}: dy must have x's shape")
+    dx = torch.empty_like(x) if dx is None else dx
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dgamma_f32 = torch.empty(N, **f32) if dgamma_f32 is None else dgamma_f32
+    dbeta_f32 = torch.empty(N, **f32) if dbeta_f32 is None else dbeta_f32
+    _same(fn, x, gamma, dy, dx, dgamma, dbeta)
+    _check_rstd(mean, M, x.device)
+    _check_rstd(rstd, M, x.device)
+    for name, t in (("dgamma_f32", dgamma_f32), ("dbeta_f32", dbeta_f32)):
+        if t.dtype != torch.float32 or t.numel() != N:
+            raise ValueError(f"{fn}: {name} must be float32 of N elements")
+    for name, t in (("dgamma", dgamma), ("dbeta", dbeta)):
+        if t is not None and t.numel() != N:
+            raise ValueError(f"{fn}: {name} must have N elements")
+    need = layernorm_bwd_workspace_bytes(M, N, dt, flags)
+    if workspace is None:
+        workspace = _cached_workspace(x.device, need)
+    st = _on_device(x.device, lambda: lib().layernorm_bwd(
+        _p(x2), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32), _p(dbeta_f32), _p(dgamma),
+        _p(dbeta), _p(workspace), workspace.numel(), M, N, dt, int(flags), _stream(x.device)))
+    _raise_on(fn, st)
+    return dx, dgamma_f32, dbeta_f32, dgamma, dbeta
+
+
+from .autograd import (FusedAddRMSNormFunction, LayerNormFunction, RMSNormFunction,  # noqa: E402,F401
+                       fused_add_rmsnorm, layer_norm, rmsnorm)

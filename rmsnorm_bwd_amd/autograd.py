@@ -1,10 +1,10 @@
 """Autograd wrappers over the C ABI binding.
 
-``rmsnorm(x, weight, eps)`` and ``fused_add_rmsnorm(x, residual, weight, eps,
-prenorm=True)`` are differentiable: their forward runs the library's forward
-that saves rstd, their backward runs the library's backward. Like the rest
-of the package they only marshal arguments; every step runs in the HIP
-kernels.
+``rmsnorm(x, weight, eps)``, ``fused_add_rmsnorm(x, residual, weight, eps,
+prenorm=True)`` and ``layer_norm(x, weight, bias, eps)`` are differentiable:
+their forward runs the library's forward that saves the row statistics, their
+backward runs the library's backward. Like the rest of the package they only
+marshal arguments; every step runs in the HIP kernels.
 
 Pages cited, by title:
   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
@@ -12,6 +12,8 @@ Pages cited, by title:
          tasks, item 3: an autograd Function whose forward saves x, weight
          and rstd and whose backward calls the backward kernel; item 4: the
          gradient with respect to residual_out for the fused-add path.
+         PR sequence and status updates: the LayerNorm follow-up's
+         LayerNormFunction (forward saving mean and rstd; dx, dgamma, dbias).
   [P800] FlyDSL PR #800, "[rmsnorm] Add fused-add / residual backward (PR
          2/3, #769)" - PR-1 commit: RMSNormFunction and a public
          rmsnorm(x, weight, eps) over inputs of any rank (rows are the last
@@ -22,7 +24,8 @@ Pages cited, by title:
 """
 import torch
 
-from . import fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, rmsnorm_bwd, rmsnorm_fwd_rstd
+from . import (fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, layernorm_bwd, layernorm_fwd_stats,
+               rmsnorm_bwd, rmsnorm_fwd_rstd)
 
 
 def _weight_grad(dgamma_f32, dgamma, weight):
@@ -91,3 +94,38 @@ def fused_add_rmsnorm(x, residual, weight, eps=1e-6, prenorm=True):
         raise ValueError(f"fused_add_rmsnorm: x.shape[-1]={x.shape[-1]} != weight length {weight.numel()}")
     out, residual_out = FusedAddRMSNormFunction.apply(x, residual, weight, eps)
     return (out, residual_out) if prenorm else out
+
+
+class LayerNormFunction(torch.autograd.Function):
+    """y = (x - mean) * rstd * weight + bias over the last dimension."""
+
+    @staticmethod
+    def forward(ctx, x, weight, bias, eps):
+        x = x.contiguous()
+        weight = weight.contiguous()
+        bias = None if bias is None else bias.contiguous()
+        y, mean, rstd = layernorm_fwd_stats(x, weight, bias, eps)
+        ctx.save_for_backward(x, weight, mean, rstd)
+        ctx.has_bias = bias is not None
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, weight, mean, rstd = ctx.saved_tensors
+        half = weight.dtype != torch.float32
+        dgamma = torch.empty_like(weight) if half else None
+        dbeta = torch.empty_like(weight) if half and ctx.has_bias else None
+        dx, dg32, db32, dgamma, dbeta = layernorm_bwd(x, weight, dy.contiguous(), mean, rstd,
+                                                      dgamma=dgamma, dbeta=dbeta)
+        dbias = None
+        if ctx.has_bias:
+            dbias = db32 if not half else dbeta
+        return dx, _weight_grad(dg32, dgamma, weight), dbias, None
+
+
+def layer_norm(x, weight, bias=None, eps=1e-5):
+    """Differentiable LayerNorm over the last dimension of x (any rank)."""
+    N = x.shape[-1]
+    if weight.numel() != N or (bias is not None and bias.numel() != N):
+        raise ValueError(f"layer_norm: weight and bias must have x.shape[-1]={N} elements")
+    return LayerNormFunction.apply(x, weight, bias, eps)

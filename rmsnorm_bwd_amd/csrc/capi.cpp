@@ -7,6 +7,9 @@
 //   [P800] FlyDSL PR #800, "[rmsnorm] Add fused-add / residual backward
 //          (PR 2/3, #769)" - review-fix commit (shape/contiguity checks,
 //          device guard) and fused-add commit (one dtype for all operands).
+// The LayerNorm entry points follow [I769]'s PR sequence and status updates
+// (forward saving mean and rstd, backward with dbias; weight and bias length
+// checks and fp32 statistics).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -75,24 +78,38 @@ int resolve_mode(unsigned flags, int64_t grid) {
     return rmsn::DG_PARTIAL;
 }
 
-size_t workspace_for(int64_t M, int64_t N, int dtype, unsigned flags, bool vector_ok) {
+size_t workspace_for(int64_t M, int64_t N, int dtype, unsigned flags, bool vector_ok, int narrays) {
     RowPlan p;
     if (!rmsn::plan_rows(N, esize(dtype), vector_ok, &p)) return 0;
     int64_t grid = rmsn::bwd_blocks(M, p);
-    return rmsn::bwd_workspace(M, N, p, resolve_mode(flags, grid));
+    return rmsn::bwd_workspace(M, N, p, resolve_mode(flags, grid), narrays);
 }
 
-int bwd_common(const void *x, const void *gamma, const void *dy, const void *dres, const float *rstd,
-               void *dx, float *dgamma_f32, void *dgamma, void *workspace, size_t workspace_bytes,
-               int64_t M, int64_t N, int dtype, unsigned flags, void *stream) {
+// The public workspace query: alignment is not known here, so it answers for
+// whichever row plan needs more.
+size_t workspace_query(int64_t M, int64_t N, int dtype, unsigned flags, int narrays) {
+    if (!dtype_ok(dtype) || check_shape(M, N) || check_flags(flags)) return 0;
+    size_t a = workspace_for(M, N, dtype, flags, true, narrays);
+    size_t b = workspace_for(M, N, dtype, flags, false, narrays);
+    return a > b ? a : b;
+}
+
+// Backward of RMSNorm (mean == NULL) or LayerNorm (mean != NULL, with
+// dbeta_f32 / dbeta).
+int bwd_common(const void *x, const void *gamma, const void *dy, const void *dres, const float *mean,
+               const float *rstd, void *dx, float *dgamma_f32, void *dgamma, float *dbeta_f32, void *dbeta,
+               void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
+               void *stream, bool layer) {
     if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
     if (int st = check_shape(M, N)) return st;
     if (int st = check_flags(flags)) return st;
     if (!gamma || !dgamma_f32 || !workspace) return RMSN_ERR_NULL;
+    if (layer && !dbeta_f32) return RMSN_ERR_NULL;
     if (M > 0 && (!x || !dy || !rstd || !dx)) return RMSN_ERR_NULL;
+    if (layer && M > 0 && !mean) return RMSN_ERR_NULL;
     const int es = esize(dtype);
-    if (!all_aligned({x, gamma, dy, dres, dx, dgamma}, es) || !all_aligned({rstd, dgamma_f32}, 4) ||
-        !aligned(workspace, 256))
+    if (!all_aligned({x, gamma, dy, dres, dx, dgamma, dbeta}, es) ||
+        !all_aligned({rstd, mean, dgamma_f32, dbeta_f32}, 4) || !aligned(workspace, 256))
         return RMSN_ERR_ALIGN;
     const bool vector_ok = all_aligned({x, gamma, dy, dres, dx}, 16);
     RowPlan p;
@@ -101,20 +118,26 @@ int bwd_common(const void *x, const void *gamma, const void *dy, const void *dre
     const int mode = resolve_mode(flags, grid);
     // the public query's answer, whatever plan the pointers select, so a
     // buffer sized by the query is always accepted and nothing less is
-    if (workspace_bytes < rmsnorm_bwd_workspace_bytes(M, N, dtype, flags)) return RMSN_ERR_WORKSPACE;
+    if (workspace_bytes < workspace_query(M, N, dtype, flags, layer ? 2 : 1)) return RMSN_ERR_WORKSPACE;
     if (flags & RMSN_CHECK_DEVICE) {
-        if (int st = check_device({x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace})) return st;
+        if (int st = check_device({x, gamma, dy, dres, mean, rstd, dx, dgamma_f32, dgamma, dbeta_f32, dbeta,
+                                   workspace}))
+            return st;
     }
     rmsn::BwdArgs a;
     a.x = x;
     a.gamma = gamma;
     a.dy = dy;
-    a.dres = dres;
+    a.dres = layer ? nullptr : dres;
     a.rstd = rstd;
+    a.mean = layer ? mean : nullptr;
     a.dx = dx;
     a.partials = nullptr;
     a.dgamma_f32 = dgamma_f32;
     a.dgamma = dgamma;
+    a.dbeta_f32 = layer ? dbeta_f32 : nullptr;
+    a.dbeta = layer ? dbeta : nullptr;
+    a.layer = layer;
     a.M = M;
     a.N = (int)N;
     a.mode = mode;
@@ -131,26 +154,32 @@ int64_t fwd_blocks(int64_t M, const RowPlan &p) {
     return steps < cap ? steps : cap;
 }
 
-int fwd_common(const void *x, const void *residual, const void *gamma, void *y, void *residual_out,
-               float *rstd, int64_t M, int64_t N, float eps, int dtype, void *stream, bool fused) {
+// Forward of RMSNorm (plain or fused-add) or, with `layer`, LayerNorm (beta
+// nullable, mean saved).
+int fwd_common(const void *x, const void *residual, const void *gamma, const void *beta, void *y,
+               void *residual_out, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+               void *stream, bool fused, bool layer) {
     if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
     if (int st = check_shape(M, N)) return st;
     if (int st = check_eps(eps)) return st;
     if (!gamma) return RMSN_ERR_NULL;
     if (M > 0 && (!x || !y || !rstd)) return RMSN_ERR_NULL;
     if (fused && M > 0 && (!residual || !residual_out)) return RMSN_ERR_NULL;
+    if (layer && M > 0 && !mean) return RMSN_ERR_NULL;
     const int es = esize(dtype);
-    if (!all_aligned({x, residual, gamma, y, residual_out}, es) || !all_aligned({rstd}, 4))
+    if (!all_aligned({x, residual, gamma, beta, y, residual_out}, es) || !all_aligned({rstd, mean}, 4))
         return RMSN_ERR_ALIGN;
-    const bool vector_ok = all_aligned({x, residual, gamma, y, residual_out}, 16);
+    const bool vector_ok = all_aligned({x, residual, gamma, beta, y, residual_out}, 16);
     RowPlan p;
     if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
     rmsn::FwdArgs a;
     a.x = x;
     a.residual = fused ? residual : nullptr;
     a.gamma = gamma;
+    a.beta = layer ? beta : nullptr;
     a.y = y;
     a.residual_out = fused ? residual_out : nullptr;
+    a.mean = layer ? mean : nullptr;
     a.rstd = rstd;
     a.M = M;
     a.N = (int)N;
@@ -165,36 +194,50 @@ extern "C" {
 
 int rmsnorm_fwd_rstd(const void *x, const void *gamma, void *y, float *rstd, int64_t M, int64_t N, float eps,
                      int dtype, void *stream) {
-    return fwd_common(x, nullptr, gamma, y, nullptr, rstd, M, N, eps, dtype, stream, false);
+    return fwd_common(x, nullptr, gamma, nullptr, y, nullptr, nullptr, rstd, M, N, eps, dtype, stream, false,
+                      false);
 }
 
 int fused_add_rmsnorm_fwd_rstd(const void *x, const void *residual, const void *gamma, void *out,
                                void *residual_out, float *rstd, int64_t M, int64_t N, float eps, int dtype,
                                void *stream) {
-    return fwd_common(x, residual, gamma, out, residual_out, rstd, M, N, eps, dtype, stream, true);
+    return fwd_common(x, residual, gamma, nullptr, out, residual_out, nullptr, rstd, M, N, eps, dtype, stream,
+                      true, false);
 }
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags) {
-    if (!dtype_ok(dtype) || check_shape(M, N) || check_flags(flags)) return 0;
-    // alignment is not known here: answer for whichever row plan needs more
-    size_t a = workspace_for(M, N, dtype, flags, true);
-    size_t b = workspace_for(M, N, dtype, flags, false);
-    return a > b ? a : b;
+    return workspace_query(M, N, dtype, flags, 1);
 }
 
 int rmsnorm_bwd(const void *x, const void *gamma, const void *dy, const float *rstd, void *dx,
                 float *dgamma_f32, void *dgamma, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int dtype, unsigned flags, void *stream) {
-    return bwd_common(x, gamma, dy, nullptr, rstd, dx, dgamma_f32, dgamma, workspace, workspace_bytes, M, N,
-                      dtype, flags, stream);
+    return bwd_common(x, gamma, dy, nullptr, nullptr, rstd, dx, dgamma_f32, dgamma, nullptr, nullptr, workspace,
+                      workspace_bytes, M, N, dtype, flags, stream, false);
 }
 
 int fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *dy, const void *dresidual_out,
                           const float *rstd, void *dx, float *dgamma_f32, void *dgamma, void *workspace,
                           size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
                           void *stream) {
-    return bwd_common(added, gamma, dy, dresidual_out, rstd, dx, dgamma_f32, dgamma, workspace,
-                      workspace_bytes, M, N, dtype, flags, stream);
+    return bwd_common(added, gamma, dy, dresidual_out, nullptr, rstd, dx, dgamma_f32, dgamma, nullptr, nullptr,
+                      workspace, workspace_bytes, M, N, dtype, flags, stream, false);
+}
+
+int layernorm_fwd_stats(const void *x, const void *gamma, const void *beta, void *y, float *mean, float *rstd,
+                        int64_t M, int64_t N, float eps, int dtype, void *stream) {
+    return fwd_common(x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, dtype, stream, false, true);
+}
+
+size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags) {
+    return workspace_query(M, N, dtype, flags, 2);
+}
+
+int layernorm_bwd(const void *x, const void *gamma, const void *dy, const float *mean, const float *rstd,
+                  void *dx, float *dgamma_f32, float *dbeta_f32, void *dgamma, void *dbeta, void *workspace,
+                  size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags, void *stream) {
+    return bwd_common(x, gamma, dy, nullptr, mean, rstd, dx, dgamma_f32, dgamma, dbeta_f32, dbeta, workspace,
+                      workspace_bytes, M, N, dtype, flags, stream, true);
 }
 
 const char *rmsn_status_string(int status) {

@@ -56,6 +56,38 @@ __device__ __forceinline__ float row_sum(float v, float *slots, int parity) {
     }
 }
 
+// Sums of two values over the tpr threads of a row group, with the same
+// one-barrier exchange as row_sum; `slots` then holds 4 * rpb * (tpr / 64)
+// floats.
+template <int TPR, int BLOCK>
+__device__ __forceinline__ void row_sum2(float &u, float &v, float *slots, int parity) {
+    if constexpr (TPR <= 64) {
+        u = group_sum<TPR>(u);
+        v = group_sum<TPR>(v);
+    } else {
+        constexpr int WPR = TPR / 64;
+        constexpr int RPB = BLOCK / TPR;
+        u = group_sum<64>(u);
+        v = group_sum<64>(v);
+        const int wave = threadIdx.x >> 6;
+        const int grp = threadIdx.x / TPR;
+        float *s = slots + 2 * (parity * (RPB * WPR) + grp * WPR);
+        if (__lane_id() == 0) {
+            s[2 * (wave % WPR)] = u;
+            s[2 * (wave % WPR) + 1] = v;
+        }
+        __syncthreads();
+        float a = s[0], b = s[1];
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) {
+            a += s[2 * w];
+            b += s[2 * w + 1];
+        }
+        u = a;
+        v = b;
+    }
+}
+
 // Byte address of element `elem` of a tensor, as an integer: window bases may
 // lie past the end of a tensor when the window holds no row (its descriptor
 // range is then empty and nothing is accessed).
@@ -79,6 +111,9 @@ __device__ __forceinline__ void partial_store(V v, V *p) {
 #endif
 }
 
+// The operation a row kernel instance computes.
+enum : int { OP_RMS = 0, OP_RMS_FUSED = 1, OP_LN = 2 };
+
 // Rows of the window starting at row wb that exist: min(RPB, M - wb), >= 0.
 template <int RPB>
 __device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
@@ -101,15 +136,18 @@ __device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
 // that keeps the compiler's memory-counter waits exact, so a window's use
 // never waits on the loads of the windows behind it.
 // ---------------------------------------------------------------------------
-template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, bool FUSED>
+template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, int OP>
 __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
+    constexpr bool FUSED = OP == OP_RMS_FUSED;
+    constexpr bool LN = OP == OP_LN;
+    constexpr int NA = LN ? 2 : 1;  // weight-gradient arrays: dgamma, and dbeta for LayerNorm
     constexpr int ES = ElemSize<DT>::value;
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
     extern __shared__ float lds[];
     float *slots = lds;
-    float *comb = lds + 2 * RPB * WPR;
+    float *comb = lds + 2 * NA * RPB * WPR;
 
     const int N = a.N;
     const int64_t M = a.M;
@@ -135,19 +173,22 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) gp[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k]);
     }
-    float acc[K][VEC];
+    // acc[0] folds dy * x_hat (dgamma), acc[1] dy (dbeta, LayerNorm)
+    float acc[NA][K][VEC];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+    for (int q = 0; q < NA; ++q)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[k][e] = 0.f;
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[q][k][e] = 0.f;
 
     P xs[DEPTH][K], ds[DEPTH][K], rs[DEPTH][FUSED ? K : 1];
-    float rr[DEPTH];
+    float rr[DEPTH], mr[DEPTH];  // rstd, and the mean for LayerNorm
 
     const int64_t wstride = (int64_t)gridDim.x * RPB;
     const int64_t w0 = (int64_t)blockIdx.x * RPB;
 
-    auto load_window = [&](int64_t wb, P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float &r) {
+    auto load_window = [&](int64_t wb, P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float &r, float &mu) {
         const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
         const rsrc_t rx = make_rsrc(at(a.x, wb * N, ES), bytes);
         const rsrc_t rd = make_rsrc(at(a.dy, wb * N, ES), bytes);
@@ -163,42 +204,74 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         }
         const rsrc_t rt = make_rsrc(at(a.rstd, wb, 4), rows_in<RPB>(wb, M) * 4u);
         r = buf_load_f32(rt, (uint32_t)grp * 4u);
+        if constexpr (LN) {
+            const rsrc_t rm = make_rsrc(at(a.mean, wb, 4), rows_in<RPB>(wb, M) * 4u);
+            mu = buf_load_f32(rm, (uint32_t)grp * 4u);
+        } else {
+            mu = 0.f;
+        }
     };
 
     // The same arithmetic as the definition, with the per-row factors pulled
-    // out of the per-element work: sum x_hat*wdy = r * sum x*wdy, and
-    // dx = (wdy - x_hat*c1) * r = r*wdy - (r*r*c1)*x. The window's dx is packed
-    // into `out`; the caller issues the next window's loads before the stores
-    // (see the loop below).
-    auto compute = [&](P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, int parity, P (&out)[K]) {
-        float part = 0.f;
+    // out of the per-element work. RMSNorm: sum x_hat*wdy = r * sum x*wdy,
+    // and dx = (wdy - x_hat*c1) * r = r*wdy - (r*r*c1)*x. LayerNorm, with
+    // xc = x - mean: c1 = r * sum xc*wdy / N, c2 = sum wdy / N (both sums in
+    // one exchange), dx = (wdy - x_hat*c1 - c2) * r = r*wdy - (r*r*c1)*xc -
+    // r*c2. Every row sum flips `parity`. The window's dx is packed into
+    // `out`; the caller issues the next window's loads before the stores (see
+    // the loop below).
+    auto compute = [&](P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, float mu, int &parity,
+                       P (&out)[K]) {
+        float b, d = 0.f;
+        if constexpr (LN) {
+            float p1 = 0.f, p2 = 0.f;
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+            for (int k = 0; k < K; ++k)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) part = fmaf(elem(xv[k], e), elem(dv[k], e) * elem(gp[k], e), part);
-        const float c1 = row_sum<TPR, BLOCK>(part, slots, parity) * r / (float)N;
-        const float b = r * r * c1;
+                for (int e = 0; e < VEC; ++e) {
+                    const float wd = elem(dv[k], e) * elem(gp[k], e);
+                    p1 = fmaf(elem(xv[k], e) - mu, wd, p1);
+                    p2 += wd;
+                }
+            row_sum2<TPR, BLOCK>(p1, p2, slots, parity);
+            parity ^= 1;
+            const float c1 = p1 * r / (float)N;
+            b = r * r * c1;
+            d = r * (p2 / (float)N);
+        } else {
+            float part = 0.f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) part = fmaf(elem(xv[k], e), elem(dv[k], e) * elem(gp[k], e), part);
+            const float c1 = row_sum<TPR, BLOCK>(part, slots, parity) * r / (float)N;
+            parity ^= 1;
+            b = r * r * c1;
+        }
         // Recompute from the packed row below instead of keeping 2 * K * VEC
         // fp32 values live across the sum.
 #pragma unroll
         for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
-        // The same for rstd. Passing its ring register through an in-place
-        // asm also keeps the register allocator from moving the slot's next
-        // rstd into a different register, which would need a copy, and a
-        // wait for that load, at the loop's back edge.
-        float r2 = r;
+        // The same for rstd (and the mean). Passing its ring register through
+        // an in-place asm also keeps the register allocator from moving the
+        // slot's next rstd into a different register, which would need a
+        // copy, and a wait for that load, at the loop's back edge.
+        float r2 = r, mu2 = mu;
         asm volatile("" : "+v"(r2));
+        if constexpr (LN) asm volatile("" : "+v"(mu2));
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             float o[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const float xv_e = elem(xv[k], e);
+                const float xv_e = LN ? elem(xv[k], e) - mu2 : elem(xv[k], e);
                 const float dyv = elem(dv[k], e);
-                float d = fmaf(-b, xv_e, r2 * (dyv * elem(gp[k], e)));
-                if constexpr (FUSED) d += elem(rv[k], e);
-                o[e] = d;
-                acc[k][e] = fmaf(dyv, xv_e * r2, acc[k][e]);
+                float dd = fmaf(-b, xv_e, r2 * (dyv * elem(gp[k], e)));
+                if constexpr (LN) dd -= d;
+                if constexpr (FUSED) dd += elem(rv[k], e);
+                o[e] = dd;
+                acc[0][k][e] = fmaf(dyv, xv_e * r2, acc[0][k][e]);
+                if constexpr (LN) acc[NA - 1][k][e] += dyv;
             }
             out[k] = make_pack<DT, VEC>(o);
         }
@@ -218,7 +291,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     // the two pessimistically and waits for windows a step does not use.
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) {
-        load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s]);
+        load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s], mr[s]);
         asm volatile("" ::: "memory");
     }
     int parity = 0;
@@ -236,10 +309,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         for (int s = 0; s < DEPTH; ++s) {
             const int64_t wb = base + s * wstride;
             P out[K];
-            compute(xs[s], ds[s], rs[s], rr[s], parity, out);
-            parity ^= 1;
+            compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out);
             settle(out);
-            load_window(wb + DEPTH * wstride, xs[s], ds[s], rs[s], rr[s]);
+            load_window(wb + DEPTH * wstride, xs[s], ds[s], rs[s], rr[s], mr[s]);
             store_dx(wb, out);
         }
     }
@@ -263,77 +335,93 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         const int64_t wb = base + s * wstride;
         if (wb < M) {
             P out[K];
-            compute(xs[s], ds[s], rs[s], rr[s], parity, out);
-            parity ^= 1;
+            compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out);
             store_dx(wb, out);
         }
     }
 
-    // ---- this block's dgamma partial ----
-    // Partials go to the workspace in 16-byte stores where the columns allow.
-    auto emit1 = [&](int j, float v) {
+    // ---- this block's weight-gradient partials (dgamma; dbeta for LayerNorm) ----
+    // Partials go to the workspace in 16-byte stores where the columns allow;
+    // array q of the tiled partials starts q * pstride floats in.
+    const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * gridDim.x;
+    auto emit1 = [&](int q, int j, float v) {
+        float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
+        void *outT = q ? a.dbeta : a.dgamma;
         if (a.mode == DG_PARTIAL) {
-            partial_store(v, a.partials + partial_index(j, blockIdx.x, gridDim.x));
+            partial_store(v, a.partials + q * pstride + partial_index(j, blockIdx.x, gridDim.x));
         } else if (a.mode == DG_ATOMIC) {
-            unsafeAtomicAdd(a.dgamma_f32 + j, v);
+            unsafeAtomicAdd(out32 + j, v);
         } else {
-            a.dgamma_f32[j] = v;
-            if (a.dgamma) {
+            out32[j] = v;
+            if (outT) {
                 if constexpr (DT == DT_F32) {
-                    static_cast<float *>(a.dgamma)[j] = v;
+                    static_cast<float *>(outT)[j] = v;
                 } else {
-                    static_cast<uint16_t *>(a.dgamma)[j] = pack1<DT>(v);
+                    static_cast<uint16_t *>(outT)[j] = pack1<DT>(v);
                 }
             }
         }
     };
     // four consecutive columns j..j+3 (j a multiple of 4, all < N) lie in one
     // partial tile, so one 16-byte store writes them
-    auto emit4 = [&](int j, float v0, float v1, float v2, float v3) {
+    auto emit4 = [&](int q, int j, float v0, float v1, float v2, float v3) {
         if (a.mode == DG_PARTIAL) {
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             f32x4 v = {v0, v1, v2, v3};
-            partial_store(v, reinterpret_cast<f32x4 *>(a.partials + partial_index(j, blockIdx.x, gridDim.x)));
+            partial_store(v, reinterpret_cast<f32x4 *>(a.partials + q * pstride +
+                                                       partial_index(j, blockIdx.x, gridDim.x)));
         } else {
-            emit1(j, v0);
-            emit1(j + 1, v1);
-            emit1(j + 2, v2);
-            emit1(j + 3, v3);
+            emit1(q, j, v0);
+            emit1(q, j + 1, v1);
+            emit1(q, j + 2, v2);
+            emit1(q, j + 3, v3);
         }
     };
     if constexpr (RPB == 1) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int c = lt + k * TPR;
-            if (c < nchunk) {
-                if constexpr (VEC % 4 == 0) {
+        for (int q = 0; q < NA; ++q)
 #pragma unroll
-                    for (int e = 0; e < VEC; e += 4)
-                        emit4(c * VEC + e, acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]);
-                } else {
+            for (int k = 0; k < K; ++k) {
+                const int c = lt + k * TPR;
+                if (c < nchunk) {
+                    if constexpr (VEC % 4 == 0) {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) emit1(c * VEC + e, acc[k][e]);
+                        for (int e = 0; e < VEC; e += 4)
+                            emit4(q, c * VEC + e, acc[q][k][e], acc[q][k][e + 1], acc[q][k][e + 2],
+                                  acc[q][k][e + 3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) emit1(q, c * VEC + e, acc[q][k][e]);
+                    }
                 }
             }
-        }
     } else {
-        // fold the rpb row groups in a fixed order, then write the block's row
+        // fold the rpb row groups in a fixed order, then write the block's rows
+        constexpr int CS = TPR * K * VEC;  // floats of one array's combine area
         for (int gi = 0; gi < RPB; ++gi) {
             if (grp == gi) {
 #pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const int c = lt + k * TPR;
-                    if (c < nchunk)
+                for (int q = 0; q < NA; ++q)
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e)
-                            comb[c * VEC + e] = gi == 0 ? acc[k][e] : comb[c * VEC + e] + acc[k][e];
-                }
+                    for (int k = 0; k < K; ++k) {
+                        const int c = lt + k * TPR;
+                        if (c < nchunk)
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) {
+                                float *cq = comb + q * CS + c * VEC + e;
+                                *cq = gi == 0 ? acc[q][k][e] : *cq + acc[q][k][e];
+                            }
+                    }
             }
             __syncthreads();
         }
         const int n4 = N & ~3;
-        for (int j = threadIdx.x * 4; j < n4; j += BLOCK * 4) emit4(j, comb[j], comb[j + 1], comb[j + 2], comb[j + 3]);
-        for (int j = n4 + threadIdx.x; j < N; j += BLOCK) emit1(j, comb[j]);
+#pragma unroll
+        for (int q = 0; q < NA; ++q) {
+            const float *cq = comb + q * CS;
+            for (int j = threadIdx.x * 4; j < n4; j += BLOCK * 4) emit4(q, j, cq[j], cq[j + 1], cq[j + 2], cq[j + 3]);
+            for (int j = n4 + threadIdx.x; j < N; j += BLOCK) emit1(q, j, cq[j]);
+        }
     }
 }
 
@@ -352,11 +440,17 @@ constexpr int FIN_LOADS = (BWD_MAX_BLOCKS + FIN_TILE - 1) / FIN_TILE;
 template <int DT>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float *__restrict__ partials, int G, int N,
                                                            float *__restrict__ dgamma_f32,
-                                                           void *__restrict__ dgamma) {
+                                                           void *__restrict__ dgamma,
+                                                           float *__restrict__ dbeta_f32,
+                                                           void *__restrict__ dbeta) {
+    // blockIdx.y selects the partial array: 0 dgamma, 1 dbeta (LayerNorm)
     __shared__ float red[FIN_TILE][FIN_TILE];
     const int c = threadIdx.x % FIN_TILE;
     const int r0 = threadIdx.x / FIN_TILE;
-    const float *tile = partials + (int64_t)blockIdx.x * G * FIN_TILE;
+    const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * G;
+    const float *tile = partials + blockIdx.y * pstride + (int64_t)blockIdx.x * G * FIN_TILE;
+    float *out32 = blockIdx.y ? dbeta_f32 : dgamma_f32;
+    void *outT = blockIdx.y ? dbeta : dgamma;
     float v[FIN_LOADS];
 #pragma unroll
     for (int k = 0; k < FIN_LOADS; ++k) {
@@ -373,12 +467,12 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float *__restri
         float sum = red[0][c];
 #pragma unroll
         for (int w = 1; w < FIN_TILE; ++w) sum += red[w][c];
-        dgamma_f32[col] = sum;
-        if (dgamma) {
+        out32[col] = sum;
+        if (outT) {
             if constexpr (DT == DT_F32) {
-                static_cast<float *>(dgamma)[col] = sum;
+                static_cast<float *>(outT)[col] = sum;
             } else {
-                static_cast<uint16_t *>(dgamma)[col] = pack1<DT>(sum);
+                static_cast<uint16_t *>(outT)[col] = pack1<DT>(sum);
             }
         }
     }
@@ -406,11 +500,17 @@ __global__ __launch_bounds__(256) void cast_kernel(const float *__restrict__ src
 // commit (added = x + residual is residual_out, rstd is that of added).
 //   a = x, or round(x + residual) for the fused variant (fp32 sum, one RNE)
 //   rstd = 1 / sqrt(sum a^2 / N + eps);   y = a * rstd * gamma
+// LayerNorm ([I769] PR sequence and status updates: the forward saves mean
+// and rstd), in two row sums over the row held in registers:
+//   mean = sum x / N, rstd = 1 / sqrt(sum (x - mean)^2 / N + eps),
+//   y = (x - mean) * rstd * gamma + beta
 // Same windows, ring and buffer descriptors as the backward.
 // ---------------------------------------------------------------------------
-template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, bool FUSED>
+template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, int OP>
 __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
     using P = Pack<DT, VEC>;
+    constexpr bool FUSED = OP == OP_RMS_FUSED;
+    constexpr bool LN = OP == OP_LN;
     constexpr int ES = ElemSize<DT>::value;
     constexpr int RPB = BLOCK / TPR;
     extern __shared__ float lds[];
@@ -429,11 +529,17 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         const int c = lt + k * TPR;
         coff[k] = c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
     }
-    P gp[K];
+    P gp[K], bp[LN ? K : 1];
     {
         const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) gp[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k]);
+        if constexpr (LN) {
+            // a null beta gets an empty range: its loads read zeros
+            const rsrc_t rb = make_rsrc(a.beta, a.beta ? row_bytes : 0u);
+#pragma unroll
+            for (int k = 0; k < K; ++k) bp[k] = buf_load<DT, VEC, AUX_DEFAULT>(rb, coff[k]);
+        }
     }
 
     P xs[DEPTH][K], rs[DEPTH][FUSED ? K : 1];
@@ -455,10 +561,44 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
     };
 
     // Computes the window's outputs (y packed into `yo`, added into `av`)
-    // and stores rstd; y and residual_out are stored by the caller after it
-    // has issued the loads that refill the ring slot.
-    auto compute = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1], int parity, P (&av)[K], P (&yo)[K]) {
+    // and stores rstd (and the mean); y and residual_out are stored by the
+    // caller after it has issued the loads that refill the ring slot. Every
+    // row sum flips `parity`.
+    auto compute = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1], int &parity, P (&av)[K], P (&yo)[K]) {
         const uint32_t nr = rows_in<RPB>(wb, M);
+        if constexpr (LN) {
+            float s1 = 0.f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) s1 += elem(xv[k], e);
+            const float mu = row_sum<TPR, BLOCK>(s1, lds, parity) / (float)N;
+            parity ^= 1;
+            float s2 = 0.f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    // chunks past the row end hold zeros but are not part of it
+                    const float dv = coff[k] == OOB ? 0.f : elem(xv[k], e) - mu;
+                    s2 = fmaf(dv, dv, s2);
+                }
+            const float var = row_sum<TPR, BLOCK>(s2, lds, parity) / (float)N;
+            parity ^= 1;
+            const float r = 1.0f / sqrtf(var + a.eps);
+            buf_store_f32(make_rsrc(at(a.rstd, wb, 4), nr * 4u), rstd_off, r);
+            buf_store_f32(make_rsrc(at(a.mean, wb, 4), nr * 4u), rstd_off, mu);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float o[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    o[e] = fmaf((elem(xv[k], e) - mu) * r, elem(gp[k], e), elem(bp[k], e));
+                yo[k] = make_pack<DT, VEC>(o);
+                av[k] = xv[k];
+            }
+            return;
+        }
         float part = 0.f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -477,6 +617,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
             }
         }
         const float ms = row_sum<TPR, BLOCK>(part, lds, parity) / (float)N;
+        parity ^= 1;
         const float r = 1.0f / sqrtf(ms + a.eps);
         buf_store_f32(make_rsrc(at(a.rstd, wb, 4), nr * 4u), rstd_off, r);
 #pragma unroll
@@ -514,7 +655,6 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
             const int64_t wb = base + s * wstride;
             P av[K], yo[K];
             compute(wb, xs[s], rs[s], parity, av, yo);
-            parity ^= 1;
             settle(yo);
             load_window(wb + DEPTH * wstride, xs[s], rs[s]);
             store_rows(wb, av, yo);
@@ -533,7 +673,6 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         if (wb < M) {
             P av[K], yo[K];
             compute(wb, xs[s], rs[s], parity, av, yo);
-            parity ^= 1;
             store_rows(wb, av, yo);
         }
     }
@@ -549,13 +688,16 @@ template <int TPR> constexpr int block_of() { return block_threads(TPR); }
 // of ring, at most RMSN_DEPTH and at least one. A window costs, per row array
 // (2, or 3 for the fused variant), 8 registers per 16-byte chunk on the vector
 // path and 2 per element on the element path (the loaded bytes plus the
-// unpacked values the arithmetic keeps live). With blocks of up to 512 threads a
-// wave may use 256 VGPRs; the budget leaves room for gamma, the dgamma
-// accumulators and the arithmetic, so that no instance spills.
-template <int VEC, int TPR, int K, bool FUSED> constexpr int ring_depth() {
+// unpacked values the arithmetic keeps live). LayerNorm's second set of
+// accumulators (dbeta, one register per element held) comes out of the same
+// budget. With blocks of up to 512 threads a wave may use 256 VGPRs; the
+// budget leaves room for gamma, the accumulators and the arithmetic, so that
+// no vector-path instance spills.
+template <int VEC, int TPR, int K, int OP> constexpr int ring_depth() {
     static_assert(block_of<TPR>() <= 512, "blocks of at most 512 threads");
-    constexpr int per_window = (FUSED ? 3 : 2) * (VEC == 1 ? 2 * K : 8 * K);
-    constexpr int d = RMSN_RING_VGPRS / per_window;
+    constexpr int per_window = (OP == OP_RMS_FUSED ? 3 : 2) * (VEC == 1 ? 2 * K : 8 * K);
+    constexpr int budget = RMSN_RING_VGPRS - (OP == OP_LN ? K * VEC : 0);
+    constexpr int d = budget / per_window;
     return d < 1 ? 1 : (d > RMSN_DEPTH ? RMSN_DEPTH : d);
 }
 
@@ -564,13 +706,20 @@ static hipError_t launch_bwd_cfg(const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
-    constexpr int DF = ring_depth<VEC, TPR, K, true>();
-    constexpr int DP = ring_depth<VEC, TPR, K, false>();
-    const size_t lds = (size_t)(2 * RPB * WPR + (RPB > 1 ? TPR * K * VEC : 0)) * sizeof(float);
-    if (a.dres)
-        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DF, true>), dim3(grid), dim3(BLOCK), lds, s, a);
+    constexpr int DF = ring_depth<VEC, TPR, K, OP_RMS_FUSED>();
+    constexpr int DP = ring_depth<VEC, TPR, K, OP_RMS>();
+    constexpr int DL = ring_depth<VEC, TPR, K, OP_LN>();
+    // LDS: the row-sum slots (two values a row for LayerNorm), then one
+    // combine area per weight-gradient array when a block holds several rows
+    const int na = a.layer ? 2 : 1;
+    const size_t lds = (size_t)(2 * na * RPB * WPR + (RPB > 1 ? na * TPR * K * VEC : 0)) * sizeof(float);
+    if (a.layer)
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DL, OP_LN>), dim3(grid), dim3(BLOCK), lds, s, a);
+    else if (a.dres)
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DF, OP_RMS_FUSED>), dim3(grid), dim3(BLOCK), lds,
+                           s, a);
     else
-        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DP, false>), dim3(grid), dim3(BLOCK), lds, s, a);
+        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DP, OP_RMS>), dim3(grid), dim3(BLOCK), lds, s, a);
     return hipGetLastError();
 }
 
@@ -579,13 +728,16 @@ static hipError_t launch_fwd_cfg(const FwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
     constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
-    constexpr int DF = ring_depth<VEC, TPR, K, true>();
-    constexpr int DP = ring_depth<VEC, TPR, K, false>();
+    constexpr int DF = ring_depth<VEC, TPR, K, OP_RMS_FUSED>();
+    constexpr int DP = ring_depth<VEC, TPR, K, OP_RMS>();
+    constexpr int DL = ring_depth<VEC, TPR, K, OP_LN>();
     const size_t lds = (size_t)(2 * RPB * WPR) * sizeof(float);
-    if (a.residual)
-        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DF, true>), dim3(grid), dim3(BLOCK), lds, s, a);
+    if (a.mean)
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DL, OP_LN>), dim3(grid), dim3(BLOCK), lds, s, a);
+    else if (a.residual)
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DF, OP_RMS_FUSED>), dim3(grid), dim3(BLOCK), lds, s, a);
     else
-        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DP, false>), dim3(grid), dim3(BLOCK), lds, s, a);
+        hipLaunchKernelGGL((fwd_kernel<DT, VEC, TPR, K, BLOCK, DP, OP_RMS>), dim3(grid), dim3(BLOCK), lds, s, a);
     return hipGetLastError();
 }
 
@@ -662,37 +814,43 @@ template <int DT>
 static hipError_t launch_bwd_dt(const RowPlan &p, const BwdArgs &args, int grid, void *workspace,
                                 hipStream_t s) {
     BwdArgs a = args;
-    hipError_t e;
-    if (a.M == 0) {
-        // no rows: dgamma is zero
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((a.N + 255) / 256), dim3(256), 0, s, a.dgamma_f32, a.N);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (a.dgamma) {
-            hipLaunchKernelGGL(cast_kernel<DT>, dim3((a.N + 255) / 256), dim3(256), 0, s, a.dgamma_f32,
-                               a.dgamma, a.N);
-            return hipGetLastError();
+    const int na = a.layer ? 2 : 1;  // weight-gradient arrays: dgamma, and dbeta for LayerNorm
+    float *out32[2] = {a.dgamma_f32, a.dbeta_f32};
+    void *outT[2] = {a.dgamma, a.dbeta};
+    const dim3 vec_grid((a.N + 255) / 256);
+    // zero (and, with `cast`, round to the dtype) every weight-gradient array
+    auto zero_all = [&](bool cast) -> hipError_t {
+        for (int q = 0; q < na; ++q) {
+            hipLaunchKernelGGL(fill_zero_kernel, vec_grid, dim3(256), 0, s, out32[q], a.N);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            if (cast && outT[q]) {
+                hipLaunchKernelGGL(cast_kernel<DT>, vec_grid, dim3(256), 0, s, out32[q], outT[q], a.N);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
         }
         return hipSuccess;
-    }
+    };
+    hipError_t e;
+    if (a.M == 0) return zero_all(true);  // no rows: the weight gradients are zero
     if (a.mode == DG_PARTIAL) {
         a.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + WS_HEADER);
         if ((e = dispatch_bwd<DT>(p, a, grid, s)) != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_finalize_kernel<DT>, dim3((a.N + FIN_TILE - 1) / FIN_TILE), dim3(256), 0, s,
-                           a.partials, grid, a.N, a.dgamma_f32, a.dgamma);
+        hipLaunchKernelGGL(bwd_finalize_kernel<DT>, dim3((a.N + FIN_TILE - 1) / FIN_TILE, na), dim3(256), 0, s,
+                           a.partials, grid, a.N, a.dgamma_f32, a.dgamma, a.dbeta_f32, a.dbeta);
         return hipGetLastError();
     }
     if (a.mode == DG_ATOMIC) {
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((a.N + 255) / 256), dim3(256), 0, s, a.dgamma_f32, a.N);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = zero_all(false)) != hipSuccess) return e;
         if ((e = dispatch_bwd<DT>(p, a, grid, s)) != hipSuccess) return e;
-        if (a.dgamma) {
-            hipLaunchKernelGGL(cast_kernel<DT>, dim3((a.N + 255) / 256), dim3(256), 0, s, a.dgamma_f32,
-                               a.dgamma, a.N);
-            return hipGetLastError();
-        }
+        for (int q = 0; q < na; ++q)
+            if (outT[q]) {
+                hipLaunchKernelGGL(cast_kernel<DT>, vec_grid, dim3(256), 0, s, out32[q], outT[q], a.N);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
         return hipSuccess;
     }
-    return dispatch_bwd<DT>(p, a, grid, s);  // DG_DIRECT: one block writes dgamma itself
+    return dispatch_bwd<DT>(p, a, grid, s);  // DG_DIRECT: one block writes the gradients itself
 }
 
 hipError_t launch_bwd(int dtype, const RowPlan &p, const BwdArgs &a, int grid, void *workspace,

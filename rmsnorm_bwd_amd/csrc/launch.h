@@ -14,21 +14,27 @@ struct BwdArgs {
     const void *dy;      // (M, N)
     const void *dres;    // dresidual_out (M, N), or null
     const float *rstd;   // (M)
+    const float *mean;   // (M) for LayerNorm, else null (RMSNorm)
     void *dx;            // (M, N)
-    float *partials;     // [grid][N] fp32 block partials (partial mode), set by the launcher
+    float *partials;     // tiled fp32 block partials (partial mode), set by the launcher
     float *dgamma_f32;   // (N)
     void *dgamma;        // (N) in the dtype, or null
+    float *dbeta_f32;    // (N), LayerNorm only
+    void *dbeta;         // (N) in the dtype, or null; LayerNorm only
     int64_t M;
     int N;
     int mode;            // DG_DIRECT / DG_PARTIAL / DG_ATOMIC
+    bool layer;          // LayerNorm (mean, dbeta) rather than RMSNorm
 };
 
 struct FwdArgs {
     const void *x;         // (M, N)
     const void *residual;  // (M, N), or null for the plain forward
     const void *gamma;     // (N)
+    const void *beta;      // (N) LayerNorm bias, or null (zeros)
     void *y;               // (M, N)
     void *residual_out;    // (M, N) when residual is given
+    float *mean;           // (M) for LayerNorm, else null (RMSNorm)
     float *rstd;           // (M)
     int64_t M;
     int N;

@@ -139,12 +139,14 @@ constexpr int64_t partial_index(int64_t col, int64_t block, int64_t G) {
 }
 
 // Bytes of workspace for a backward call: a header, then the tiled fp32 block
-// partials when they are combined by the fixed-order kernel.
-inline size_t bwd_workspace(int64_t M, int64_t N, const RowPlan &p, int mode) {
+// partials, one array per weight gradient (narrays: 1 for RMSNorm's dgamma,
+// 2 for LayerNorm's dgamma and dbeta), when they are combined by the
+// fixed-order kernel.
+inline size_t bwd_workspace(int64_t M, int64_t N, const RowPlan &p, int mode, int narrays = 1) {
     size_t ws = WS_HEADER;
     if (mode == DG_PARTIAL) {
         const int64_t tiles = (N + FIN_TILE - 1) / FIN_TILE;
-        ws += (size_t)bwd_blocks(M, p) * (size_t)(tiles * FIN_TILE) * sizeof(float);
+        ws += (size_t)narrays * (size_t)bwd_blocks(M, p) * (size_t)(tiles * FIN_TILE) * sizeof(float);
     }
     return ws;
 }

@@ -75,6 +75,15 @@ def fused_bwd(**kw):
                                          a["flags"], None)
 
 
+def ln_bwd(**kw):
+    a = dict(x=A, gamma=A, dy=A, mean=A, rstd=A, dx=A, dg32=A, db32=A, dg=None, db=None, ws=A,
+             wsb=0, M=4, N=64, dtype=R.BF16, flags=0)
+    a.update(kw)
+    return R.lib().layernorm_bwd(P(a["x"]), P(a["gamma"]), P(a["dy"]), P(a["mean"]), P(a["rstd"]),
+                                 P(a["dx"]), P(a["dg32"]), P(a["db32"]), P(a["dg"]), P(a["db"]),
+                                 P(a["ws"]), a["wsb"], a["M"], a["N"], a["dtype"], a["flags"], None)
+
+
 def fwd(**kw):
     a = dict(x=A, gamma=A, y=A, rstd=A, M=0, N=64, eps=1e-5, dtype=R.BF16)
     a.update(kw)
@@ -123,6 +132,31 @@ BWD_CASES = [
 def test_bwd_validation(name, kw, want):
     assert bwd(**kw) == want
     assert fused_bwd(**kw) == want
+    assert ln_bwd(**kw) == want
+
+
+def test_layernorm_bwd_validation_of_its_own_operands():
+    assert ln_bwd(mean=None) == NULL
+    assert ln_bwd(db32=None) == NULL
+    assert ln_bwd(mean=A + 2) == ALIGN
+    assert ln_bwd(db32=A + 2) == ALIGN
+    assert ln_bwd(db=A + 1) == ALIGN
+    # no rows: the mean may be absent; still refused for the workspace size
+    assert ln_bwd(M=0, mean=None) == WORKSPACE
+    for M, N, dt in ((4096, 4096, R.BF16), (512, 3000, R.F32)):
+        need = R.layernorm_bwd_workspace_bytes(M, N, dt)
+        assert ln_bwd(M=M, N=N, dtype=dt, wsb=need - 1) == WORKSPACE
+
+
+def test_layernorm_workspace_holds_two_partial_arrays():
+    q, ql = R.rmsnorm_bwd_workspace_bytes, R.layernorm_bwd_workspace_bytes
+    assert ql(4096, 4096, R.BF16) == 256 + 2 * 256 * 4096 * 4
+    assert ql(4096, 4096, R.BF16, R.DGAMMA_ATOMIC) == 256
+    assert ql(1, 4096, R.BF16) == 256
+    for M in (1, 7, 5000):
+        for N in (1, 255, 4096, 16384):
+            assert ql(M, N, R.F32) - 256 == 2 * (q(M, N, R.F32) - 256)
+    assert ql(4, 0, R.BF16) == 0 and ql(4, 64, 9) == 0
 
 
 def test_bwd_workspace_one_byte_short():
@@ -163,6 +197,26 @@ def test_fwd_validation(name, kw, want):
 def test_fused_fwd_needs_residual():
     assert fused_fwd(M=2, res=None, out=A + 1) == NULL
     assert fused_fwd(M=2, res_out=None, out=A + 1) == NULL
+
+
+def ln_fwd(**kw):
+    a = dict(x=A, gamma=A, beta=None, y=A, mean=A, rstd=A, M=0, N=64, eps=1e-5, dtype=R.BF16)
+    a.update(kw)
+    return R.lib().layernorm_fwd_stats(P(a["x"]), P(a["gamma"]), P(a["beta"]), P(a["y"]),
+                                       P(a["mean"]), P(a["rstd"]), a["M"], a["N"], a["eps"],
+                                       a["dtype"], None)
+
+
+@pytest.mark.parametrize("name,kw,want", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_layernorm_fwd_validation(name, kw, want):
+    assert ln_fwd(**kw) == want
+
+
+def test_layernorm_fwd_own_operands():
+    assert ln_fwd(M=2, mean=None, y=A + 1) == NULL
+    assert ln_fwd(beta=A + 1) == ALIGN
+    assert ln_fwd(mean=A + 2) == ALIGN
+    assert ln_fwd(M=0) == OK
 
 
 def test_fwd_with_no_rows_is_ok_without_a_launch():

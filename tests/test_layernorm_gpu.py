@@ -1,0 +1,176 @@
+"""GPU parity of the LayerNorm forward (saving mean and rstd) and backward
+(dx, dgamma, dbeta) through the C ABI, against the CPU oracle.
+
+Shapes cover every row plan: rows inside one wavefront, two and four rows per
+block window, one to eight 16-byte chunks per thread, the element path (N not
+a multiple of the vector width, and misaligned pointers), a single row, and
+no rows. Inputs have a nonzero mean so that the mean handling matters. The
+backward reads the oracle's saved statistics, as the RMSNorm parity tests
+do; the GPU forward's statistics are checked on their own.
+
+Tolerances: y and dx as for RMSNorm (1e-5 normwise for fp32, 2e-2 plus one
+ulp element by element for half types); dgamma and dbeta 1e-4 * sqrt(M)
+normwise; rstd 1e-5 per element; the mean within 1e-6 of the row's largest
+|x| (an fp32 sum of N terms, whose error is relative to the terms, not to a
+mean that may nearly cancel).
+
+Math: FlyDSL issue #769 ("[Feature] Add rmsnorm backward (+ forward saves
+rstd) ..."), PR sequence and status updates (the LayerNorm follow-up).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_bwd_amd as R
+import workloads
+from parity_util import DEV, assert_close, empty_like_dev, place, rel, tol_dgamma
+
+pytestmark = pytest.mark.gpu
+
+T = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+CASES = [
+    ("8x256_f32", 8, 256, "f32", 1e-5),        # rows inside one wavefront
+    ("100x64_bf16", 100, 64, "bf16", 1e-5),    # 8 chunks: 16-lane groups
+    ("257x640_f16", 257, 640, "f16", 1e-5),    # four rows a window, ragged M
+    ("512x2048_bf16", 512, 2048, "bf16", 1e-5),  # two rows a window
+    ("512x3000_f32", 512, 3000, "f32", 1e-5),  # two chunks a thread, ragged chunks
+    ("4096x4096_bf16", 4096, 4096, "bf16", 1e-6),  # one row a window
+    ("1024x8192_bf16", 1024, 8192, "bf16", 1e-6),  # two chunks a thread
+    ("64x16384_f16", 64, 16384, "f16", 1e-6),  # four chunks a thread
+    ("33x16384_f32", 33, 16384, "f32", 1e-6),  # eight chunks a thread
+    ("300x1001_f32", 300, 1001, "f32", 1e-5),  # element path
+    ("1x4096_bf16", 1, 4096, "bf16", 1e-6),    # one block writes the gradients
+]
+
+
+def _inputs(M, N, dt, seed=31, with_beta=True):
+    gen = np.random.Generator(np.random.PCG64(seed))
+    td = T[dt]
+    x = workloads.normal(gen, (M, N), 0.5, 1.0, td).reshape(M, N)
+    g = workloads.normal(gen, (N,), 1.0, 0.1, td)
+    b = workloads.normal(gen, (N,), 0.0, 0.1, td) if with_beta else None
+    dy = workloads.normal(gen, (M, N), 0.0, 1e-2, td).reshape(M, N)
+    return x, g, b, dy
+
+
+def run_case(M, N, dt, eps, flags=R.DGAMMA_AUTO, misalign=False, with_beta=True, seed=31):
+    x, g, b, dy = _inputs(M, N, dt, seed, with_beta)
+    td = T[dt]
+    mean_ref, rstd_ref, y_ref = oracle.layernorm_fwd(x, g, b, eps)
+    dx_ref, dg_ref, db_ref = oracle.layernorm_bwd(x, g, dy, mean_ref, rstd_ref)
+    xg, gg, dyg = place(x, misalign), place(g, misalign), place(dy, misalign)
+    bg = place(b, misalign) if b is not None else None
+    y, mean, rstd = R.layernorm_fwd_stats(xg, gg, bg, eps, y=empty_like_dev((M, N), td, misalign))
+    dgt = torch.empty(N, dtype=td, device=DEV)
+    dbt = torch.empty(N, dtype=td, device=DEV)
+    dx, dg32, db32, dgt, dbt = R.layernorm_bwd(
+        xg, gg, dyg, mean_ref.to(DEV), rstd_ref.to(DEV), dx=empty_like_dev((M, N), td, misalign),
+        dgamma=dgt, dbeta=dbt, flags=flags)
+    torch.cuda.synchronize()
+    return dict(M=M, N=N, td=td, x=x, y=(y, y_ref), mean=(mean, mean_ref), rstd=(rstd, rstd_ref),
+                dx=(dx, dx_ref), dg=(dg32, dg_ref), db=(db32, db_ref), dgt=dgt, dbt=dbt)
+
+
+def check(c):
+    td, M = c["td"], c["M"]
+    if M > 0:
+        rstd, r_ref = c["rstd"]
+        er = ((rstd.cpu().double() - r_ref.double()).abs() / r_ref.double().abs()).max().item()
+        assert er <= 1e-5, f"rstd: error {er:.3g}"
+        mean, m_ref = c["mean"]
+        scale = c["x"].double().abs().amax(dim=1)
+        em = ((mean.cpu().double() - m_ref.double()).abs() / scale).max().item()
+        assert em <= 1e-6, f"mean: error {em:.3g}"
+        assert_close("y", c["y"][0], c["y"][1], td)
+        assert_close("dx", c["dx"][0], c["dx"][1], td)
+    for name, key, half in (("dgamma", "dg", "dgt"), ("dbeta", "db", "dbt")):
+        got, ref = c[key]
+        e = rel(got, ref)
+        assert e <= tol_dgamma(M), f"{name}: error {e:.3g} > {tol_dgamma(M):.3g}"
+        assert torch.equal(c[half].cpu(), got.cpu().to(td)), f"{name}: dtype copy is not the RNE of fp32"
+
+
+@pytest.mark.parametrize("name,M,N,dt,eps", CASES, ids=[c[0] for c in CASES])
+def test_layernorm_parity(name, M, N, dt, eps):
+    print("case layernorm", name, flush=True)
+    check(run_case(M, N, dt, eps))
+
+
+def test_layernorm_without_beta():
+    print("case layernorm no beta", flush=True)
+    check(run_case(300, 2048, "bf16", 1e-5, with_beta=False))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_layernorm_misaligned_pointers(dt):
+    print("case layernorm misaligned", dt, flush=True)
+    check(run_case(77, 1024, dt, 1e-5, misalign=True))
+
+
+def test_layernorm_deterministic_repeats_bit_for_bit():
+    print("case layernorm deterministic", flush=True)
+    M, N = 2048, 4096
+    x, g, b, dy = _inputs(M, N, "bf16")
+    mean, rstd, _ = oracle.layernorm_fwd(x, g, b, 1e-6, want_y=False)
+    args = [t.to(DEV) for t in (x, g, dy, mean, rstd)]
+    first = R.layernorm_bwd(*args, flags=R.DGAMMA_DETERMINISTIC)
+    for _ in range(3):
+        again = R.layernorm_bwd(*args, flags=R.DGAMMA_DETERMINISTIC)
+        torch.cuda.synchronize()
+        for a, b_ in zip(first[:3], again[:3]):
+            assert torch.equal(a, b_)
+
+
+def test_layernorm_atomic_mode_within_tolerance():
+    print("case layernorm atomic", flush=True)
+    check(run_case(1024, 4096, "bf16", 1e-6, flags=R.DGAMMA_ATOMIC))
+
+
+def test_layernorm_no_rows_gives_zero_gradients():
+    N = 512
+    g = torch.ones(N, dtype=torch.bfloat16, device=DEV)
+    x = torch.empty(0, N, dtype=torch.bfloat16, device=DEV)
+    empty = torch.empty(0, dtype=torch.float32, device=DEV)
+    dg32 = torch.full((N,), 7.0, device=DEV)
+    db32 = torch.full((N,), 7.0, device=DEV)
+    dgt = torch.full((N,), 7.0, dtype=torch.bfloat16, device=DEV)
+    dbt = torch.full((N,), 7.0, dtype=torch.bfloat16, device=DEV)
+    R.layernorm_bwd(x, g, x, empty, empty, dgamma_f32=dg32, dbeta_f32=db32, dgamma=dgt, dbeta=dbt)
+    torch.cuda.synchronize()
+    for t in (dg32, db32, dgt, dbt):
+        assert not t.any()
+
+
+def test_layer_norm_autograd_against_oracle_and_fp64_torch():
+    print("case layer_norm autograd", flush=True)
+    shape, N, eps = (4, 6, 768), 768, 1e-5
+    x, g, b, _ = _inputs(24, N, "bf16")
+    gen = np.random.Generator(np.random.PCG64(3))
+    up = workloads.normal(gen, (24, N), 0.0, 1e-2, torch.bfloat16).reshape(24, N)
+    xg = x.reshape(shape).to(DEV).requires_grad_()
+    wg = g.to(DEV).requires_grad_()
+    bg = b.to(DEV).requires_grad_()
+    y = R.layer_norm(xg, wg, bg, eps)
+    y.backward(up.reshape(shape).to(DEV))
+    torch.cuda.synchronize()
+    mean, rstd, y_ref = oracle.layernorm_fwd(x, g, b, eps)
+    dx_ref, dg_ref, db_ref = oracle.layernorm_bwd(x, g, up, mean, rstd)
+    assert_close("y", y.detach().reshape(24, N), y_ref, torch.bfloat16)
+    assert_close("dx", xg.grad.reshape(24, N), dx_ref, torch.bfloat16)
+    assert_close("dweight", wg.grad, dg_ref, torch.bfloat16)
+    assert_close("dbias", bg.grad, db_ref, torch.bfloat16)
+    # fp32 end to end against torch's own layer_norm autograd in fp64
+    x32 = x.float().reshape(shape)
+    xa = x32.to(DEV).requires_grad_()
+    wa = g.float().to(DEV).requires_grad_()
+    ba = b.float().to(DEV).requires_grad_()
+    R.layer_norm(xa, wa, ba, eps).backward(up.float().reshape(shape).to(DEV))
+    x64 = x32.double().requires_grad_()
+    w64 = g.double().requires_grad_()
+    b64 = b.double().requires_grad_()
+    torch.nn.functional.layer_norm(x64, (N,), w64, b64, eps).backward(up.double().reshape(shape))
+    assert rel(xa.grad.cpu(), x64.grad) <= 1e-5
+    assert rel(wa.grad.cpu(), w64.grad) <= tol_dgamma(24)
+    assert rel(ba.grad.cpu(), b64.grad) <= tol_dgamma(24)

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs and the named workloads (shapes, dtypes, eps,
 value distributions) shared by the tests and the benchmark.
 
-This module holds input generation only: no step of the RMSNorm arithmetic is
-here. Both the CPU oracle and the GPU library consume the exact bits it
+This module holds input generation only: no step of the RMSNorm or LayerNorm
+arithmetic is here. Both the CPU oracle and the GPU library consume the exact bits it
 produces.
 
 Recipe: one ``numpy.random.Generator(PCG64(seed))`` per workload; each tensor,
@@ -23,8 +23,8 @@ _CHUNK = 1 << 24
 
 @dataclass(frozen=True)
 class Workload:
-    """One named problem: op ("plain" or "fused"), shape, dtype, eps, and the
-    (mu, sigma) of every input in draw order."""
+    """One named problem: op ("plain" or "fused" RMSNorm, or "layernorm"),
+    shape, dtype, eps, and the (mu, sigma) of every input in draw order."""
     name: str
     op: str
     M: int
@@ -54,6 +54,12 @@ def _fused(name, M, N, dtype, eps):
                      ("dy", 0.0, 1e-2), ("dresidual_out", 0.0, 1e-2)))
 
 
+def _layernorm(name, M, N, dtype, eps):
+    # x with a nonzero mean, so that the mean matters
+    return Workload(name, "layernorm", M, N, dtype, eps,
+                    (("x", 0.5, 1.0), ("gamma", 1.0, 0.1), ("beta", 0.0, 0.1), ("dy", 0.0, 1e-2)))
+
+
 # The workloads the library is specified, tested and measured on.
 WORKLOADS = {w.name: w for w in (
     _plain("plain_8x256_f32", 8, 256, "f32", 1e-5, 1.0),
@@ -63,6 +69,7 @@ WORKLOADS = {w.name: w for w in (
     _fused("fused_1024x8192_bf16", 1024, 8192, "bf16", 1e-6),
     _fused("fused_32768x8192_bf16", 32768, 8192, "bf16", 1e-6),
     _plain("plain_1x4096_bf16", 1, 4096, "bf16", 1e-6, 1e-2),
+    _layernorm("layernorm_4096x4096_bf16", 4096, 4096, "bf16", 1e-6),
 )}
 
 HEADLINE = "plain_4096x4096_bf16"
@@ -89,7 +96,7 @@ def make_inputs(w, M=None, N=None, seed=None):
     gen = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     out = {}
     for name, mu, sigma in w.dists:
-        shape = (N,) if name == "gamma" else (M, N)
+        shape = (N,) if name in ("gamma", "beta") else (M, N)
         out[name] = normal(gen, shape, mu, sigma, w.torch_dtype)
     return out
 
