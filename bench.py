@@ -159,6 +159,41 @@ def latency_floor(w_name="plain_1x4096_bf16"):
             "timing": "HIP graph replay", "graph_matches_eager": bool(torch.equal(eager, s["dx"]))}
 
 
+def mode_sweep():
+    """The dgamma combining modes against each other on an (M, N) grid, GPU
+    time per call from HIP-graph replay (one JSON line per shape): the
+    measurement behind the default mode's choices."""
+    dev = torch.device("cuda:0")
+    for dt in (torch.bfloat16, torch.float32):
+        es = 2 if dt == torch.bfloat16 else 4
+        for N in (256, 1024, 4096, 8192, 16384):
+            for M in (1, 2, 8, 32, 128, 512, 2048, 8192):
+                per = 4 * M * N * es
+                nsets = max(1, min(8, -(-ROTATE_BYTES // per)))
+                g = torch.ones(N, dtype=dt, device=dev)
+                sets = []
+                for _ in range(nsets):
+                    x = torch.randn(M, N, device=dev).to(dt)
+                    _, rstd = R.rmsnorm_fwd_rstd(x, g, 1e-6)
+                    sets.append((x, torch.randn(M, N, device=dev).to(dt), rstd, torch.empty_like(x),
+                                 torch.empty(N, device=dev), torch.empty(N, dtype=dt, device=dev),
+                                 torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(M, N, dt)),
+                                             dtype=torch.uint8, device=dev)))
+                row = {"dtype": str(dt).split(".")[-1], "M": M, "N": N}
+                for name, fl in (("auto", R.DGAMMA_AUTO), ("deterministic", R.DGAMMA_DETERMINISTIC),
+                                 ("atomic", R.DGAMMA_ATOMIC)):
+                    it = iter(range(1 << 30))
+
+                    def call():
+                        t = sets[next(it) % nsets]
+                        R.rmsnorm_bwd(t[0], g, t[1], t[2], dx=t[3], dgamma_f32=t[4], dgamma=t[5],
+                                      workspace=t[6], flags=fl)
+                    row[name + "_us"] = round(_graph_us(call, calls=max(nsets, 8), replays=10), 2)
+                print(json.dumps(row), flush=True)
+                del sets
+                torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, d, calls=5):
     """The CPU oracle (fp64, single thread) on the same workload."""
     import oracle
@@ -212,6 +247,8 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE)
     ap.add_argument("--hot", action="store_true", help="time one buffer set only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--mode-sweep", action="store_true",
+                    help="time the dgamma modes on an (M, N) grid (one JSON line per shape) and exit")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the copy-bandwidth and one-row latency figures (profiled runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -222,6 +259,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(dgamma would need one all-reduce per step across GPUs).", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode_sweep:
+        mode_sweep()
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

@@ -81,7 +81,7 @@ int resolve_mode(unsigned flags, int64_t grid) {
 size_t workspace_for(int64_t M, int64_t N, int dtype, unsigned flags, bool vector_ok, int narrays) {
     RowPlan p;
     if (!rmsn::plan_rows(N, esize(dtype), vector_ok, &p)) return 0;
-    int64_t grid = rmsn::bwd_blocks(M, p);
+    int64_t grid = rmsn::bwd_blocks(M, N, p);
     return rmsn::bwd_workspace(M, N, p, resolve_mode(flags, grid), narrays);
 }
 
@@ -114,7 +114,7 @@ int bwd_common(const void *x, const void *gamma, const void *dy, const void *dre
     const bool vector_ok = all_aligned({x, gamma, dy, dres, dx}, 16);
     RowPlan p;
     if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
-    const int64_t grid = rmsn::bwd_blocks(M, p);
+    const int64_t grid = rmsn::bwd_blocks(M, N, p);
     const int mode = resolve_mode(flags, grid);
     // the public query's answer, whatever plan the pointers select, so a
     // buffer sized by the query is always accepted and nothing less is

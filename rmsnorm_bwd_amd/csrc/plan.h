@@ -118,8 +118,15 @@ constexpr int BWD_MAX_BLOCKS = RMSN_BWD_MAX_BLOCKS;
 constexpr size_t WS_HEADER = 256;
 
 // Blocks the backward launches for M rows: one block per rpb rows at small M,
-// capped so each block folds many rows into one dgamma partial.
-inline int64_t bwd_blocks(int64_t M, const RowPlan &p) {
+// capped so each block folds many rows into one dgamma partial. A problem of
+// short rows (N <= 1024) and at most 8192 elements runs in one block that
+// writes the gradients itself, saving the finalize launch: measured on
+// MI355X (kernel time, HIP-graph replay) that is 6.2 instead of 7.7 us at
+// 32 x 256 bf16 and 4.2 instead of 5.6 us at 8 x 1024, while one block
+// holding several long rows is latency-bound (64 x 4096 bf16: 39.6 us against
+// 5.4 us with 64 blocks and partials).
+inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p) {
+    if (M <= 0 || (N <= 1024 && M * N <= 8192)) return 1;
     int64_t steps = (M + p.rpb - 1) / p.rpb;
     if (steps < 1) steps = 1;
     return steps < BWD_MAX_BLOCKS ? steps : BWD_MAX_BLOCKS;
@@ -146,7 +153,7 @@ inline size_t bwd_workspace(int64_t M, int64_t N, const RowPlan &p, int mode, in
     size_t ws = WS_HEADER;
     if (mode == DG_PARTIAL) {
         const int64_t tiles = (N + FIN_TILE - 1) / FIN_TILE;
-        ws += (size_t)narrays * (size_t)bwd_blocks(M, p) * (size_t)(tiles * FIN_TILE) * sizeof(float);
+        ws += (size_t)narrays * (size_t)bwd_blocks(M, N, p) * (size_t)(tiles * FIN_TILE) * sizeof(float);
     }
     return ws;
 }

@@ -148,6 +148,17 @@ def test_layernorm_bwd_validation_of_its_own_operands():
         assert ln_bwd(M=M, N=N, dtype=dt, wsb=need - 1) == WORKSPACE
 
 
+def test_small_short_row_problems_run_in_one_block():
+    """The default mode's measured rule: rows of at most 1024 elements and at
+    most 8192 elements in all run in one block that writes dgamma itself (no
+    partials); anything larger uses per-block partials."""
+    q = R.rmsnorm_bwd_workspace_bytes
+    for M, N in ((32, 256), (8, 1024), (1, 4096), (1, 16384), (64, 128)):
+        assert q(M, N, R.BF16) == 256, (M, N)
+    for M, N in ((33, 256), (9, 1024), (2, 4096), (5, 2048)):
+        assert q(M, N, R.BF16) > 256, (M, N)
+
+
 def test_layernorm_workspace_holds_two_partial_arrays():
     q, ql = R.rmsnorm_bwd_workspace_bytes, R.layernorm_bwd_workspace_bytes
     assert ql(4096, 4096, R.BF16) == 256 + 2 * 256 * 4096 * 4

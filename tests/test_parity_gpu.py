@@ -94,6 +94,8 @@ EDGE = [
     (300, 64, "bf16"), (1000, 128, "f32"), (129, 1024, "f16"), (64, 2048, "f16"),
     (33, 8192, "bf16"), (17, 16384, "bf16"), (6, 16384, "f32"), (2, 12288, "f32"),
     (1, 16383, "bf16"), (700, 768, "bf16"), (258, 5120, "f16"),
+    # both sides of the one-block rule (N <= 1024 and M * N <= 8192)
+    (32, 256, "bf16"), (33, 256, "bf16"), (8, 1024, "f32"), (9, 1024, "f32"),
 ]
 
 
