@@ -16,7 +16,14 @@
  *     library allocates nothing, frees nothing and never synchronises.
  *   - Row tensors are (M, N), row-major and contiguous (row stride N
  *     elements); gamma, beta and the weight-gradient outputs have N
- *     elements; rstd and mean have M.
+ *     elements; rstd and mean have M. Each entry point has a *_strided twin
+ *     that takes a row stride ld (elements) per row tensor, N <= ld <=
+ *     RMSN_MAX_LD: row i of that tensor starts ld * i elements after its
+ *     base, elements inside a row stay contiguous, and the gaps between
+ *     rows are neither read nor written. Other arguments, results and
+ *     errors are those of the contiguous entry point (a stride out of range
+ *     is RMSN_ERR_SHAPE); rows take the 16-byte vector path only if every
+ *     row of every row tensor starts on a 16-byte boundary.
  *   - One element dtype (rmsn_dtype_t) covers every row tensor, gamma and
  *     beta. rstd, mean, dgamma_f32 and dbeta_f32 are always float32.
  *   - Pointers need only element alignment. Rows whose start is not 16-byte
@@ -40,6 +47,8 @@ extern "C" {
 #endif
 
 #define RMSN_MAX_N 16384
+/* Largest row stride, in elements, of the *_strided entry points. */
+#define RMSN_MAX_LD (1LL << 24)
 
 typedef enum { RMSN_F32 = 0, RMSN_F16 = 1, RMSN_BF16 = 2 } rmsn_dtype_t;
 
@@ -169,6 +178,34 @@ int layernorm_bwd(const void *x, const void *gamma, const void *dy, const float 
                   void *dx, float *dgamma_f32, float *dbeta_f32, void *dgamma, void *dbeta,
                   void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
                   unsigned flags, void *stream);
+
+/* Strided twins (row strides in elements; see the conventions above). The
+ * gaps between rows are the caller's views, e.g. a slice of wider rows, a
+ * column block of a packed tensor, or a transposed leading dimension; the
+ * pages assert contiguity ([P800] review-fix commit), which these relax. */
+int rmsnorm_fwd_rstd_strided(const void *x, int64_t ldx, const void *gamma, void *y, int64_t ldy,
+                             float *rstd, int64_t M, int64_t N, float eps, int dtype, void *stream);
+int fused_add_rmsnorm_fwd_rstd_strided(const void *x, int64_t ldx, const void *residual, int64_t ldres,
+                                       const void *gamma, void *out, int64_t ldout, void *residual_out,
+                                       int64_t ldres_out, float *rstd, int64_t M, int64_t N, float eps,
+                                       int dtype, void *stream);
+int rmsnorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy,
+                        const float *rstd, void *dx, int64_t lddx, float *dgamma_f32, void *dgamma,
+                        void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
+                        unsigned flags, void *stream);
+int fused_add_rmsnorm_bwd_strided(const void *added, int64_t ldadded, const void *gamma, const void *dy,
+                                  int64_t lddy, const void *dresidual_out, int64_t lddres,
+                                  const float *rstd, void *dx, int64_t lddx, float *dgamma_f32,
+                                  void *dgamma, void *workspace, size_t workspace_bytes, int64_t M,
+                                  int64_t N, int dtype, unsigned flags, void *stream);
+int layernorm_fwd_stats_strided(const void *x, int64_t ldx, const void *gamma, const void *beta, void *y,
+                                int64_t ldy, float *mean, float *rstd, int64_t M, int64_t N, float eps,
+                                int dtype, void *stream);
+int layernorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy,
+                          const float *mean, const float *rstd, void *dx, int64_t lddx,
+                          float *dgamma_f32, float *dbeta_f32, void *dgamma, void *dbeta,
+                          void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
+                          unsigned flags, void *stream);
 
 const char *rmsn_status_string(int status);
 

@@ -62,10 +62,22 @@ def lib():
         L.layernorm_bwd_workspace_bytes.argtypes = [I64, I64, I, U]
         L.layernorm_bwd_workspace_bytes.restype = SZ
         L.layernorm_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I, U, P]
+        L.rmsnorm_fwd_rstd_strided.argtypes = [P, I64, P, P, I64, P, I64, I64, F, I, P]
+        L.fused_add_rmsnorm_fwd_rstd_strided.argtypes = [P, I64, P, I64, P, P, I64, P, I64, P, I64, I64,
+                                                         F, I, P]
+        L.rmsnorm_bwd_strided.argtypes = [P, I64, P, P, I64, P, P, I64, P, P, P, SZ, I64, I64, I, U, P]
+        L.fused_add_rmsnorm_bwd_strided.argtypes = [P, I64, P, P, I64, P, I64, P, P, I64, P, P, P, SZ,
+                                                    I64, I64, I, U, P]
+        L.layernorm_fwd_stats_strided.argtypes = [P, I64, P, P, P, I64, P, P, I64, I64, F, I, P]
+        L.layernorm_bwd_strided.argtypes = [P, I64, P, P, I64, P, P, P, I64, P, P, P, P, P, SZ, I64,
+                                            I64, I, U, P]
         L.rmsn_status_string.argtypes = [I]
         L.rmsn_status_string.restype = ctypes.c_char_p
         for fn in ("rmsnorm_fwd_rstd", "fused_add_rmsnorm_fwd_rstd", "rmsnorm_bwd",
-                   "fused_add_rmsnorm_bwd", "layernorm_fwd_stats", "layernorm_bwd"):
+                   "fused_add_rmsnorm_bwd", "layernorm_fwd_stats", "layernorm_bwd",
+                   "rmsnorm_fwd_rstd_strided", "fused_add_rmsnorm_fwd_rstd_strided",
+                   "rmsnorm_bwd_strided", "fused_add_rmsnorm_bwd_strided",
+                   "layernorm_fwd_stats_strided", "layernorm_bwd_strided"):
             getattr(L, fn).restype = I
         _lib = L
     return _lib
@@ -97,15 +109,46 @@ def _on_device(device, fn, *args):
         return fn(*args)
 
 
+def _vec(t, N, name, what):
+    """Check a 1-D per-column tensor (gamma, beta, their gradients)."""
+    if t.dim() != 1 or t.numel() != N or not t.is_contiguous():
+        raise ValueError(f"{name}: {what} must be a contiguous 1-D tensor of N={N} elements")
+
+
+def _view(t, N, name, what):
+    """(M, ld) of a row tensor: its last dimension is the row (N elements at
+    unit stride) and its leading dimensions must collapse into one row index
+    with a single stride ld (a contiguous tensor, or a slice or column block
+    of wider rows). Anything else is refused; the caller can copy it."""
+    if t.dim() == 0 or t.shape[-1] != N:
+        raise ValueError(f"{name}: {what} must have rows of N={N} elements")
+    if N > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: {what} must have unit stride along its rows")
+    lead = [(sz, st) for sz, st in zip(t.shape[:-1], t.stride()[:-1]) if sz != 1]
+    M = 1
+    for sz, _ in lead:
+        M *= sz
+    if not lead or t.is_contiguous():
+        return M, N
+    for (sz, st), (sz2, st2) in zip(lead[:-1], lead[1:]):
+        if st != st2 * sz2:
+            raise ValueError(f"{name}: {what}'s leading dimensions do not form one row stride")
+    ld = lead[-1][1]
+    if ld < N:
+        raise ValueError(f"{name}: {what}'s rows overlap (row stride {ld} < N={N})")
+    return M, ld
+
+
 def _rows(x, gamma, name):
-    """(M, N) view of x with the pages' guards: last dim == len(gamma), contiguous."""
+    """(M, N, ldx) of x with the pages' guards: last dim == len(gamma), one dtype."""
     if gamma.dim() != 1:
         raise ValueError(f"{name}: gamma must be 1-D")
     if x.shape[-1] != gamma.shape[0]:
         raise ValueError(f"{name}: x.shape[-1]={x.shape[-1]} != len(gamma)={gamma.shape[0]}")
-    if not x.is_contiguous() or not gamma.is_contiguous():
-        raise ValueError(f"{name}: tensors must be contiguous (row-major)")
-    return x.reshape(-1, x.shape[-1])
+    N = gamma.shape[0]
+    _vec(gamma, N, name, "gamma")
+    M, ld = _view(x, N, name, "x")
+    return M, N, ld
 
 
 def _same(name, ref, *ts):
@@ -116,8 +159,15 @@ def _same(name, ref, *ts):
             raise TypeError(f"{name}: dtype mismatch {t.dtype} vs {ref.dtype}")
         if t.device != ref.device:
             raise ValueError(f"{name}: tensors on different devices")
-        if not t.is_contiguous():
-            raise ValueError(f"{name}: tensors must be contiguous (row-major)")
+
+
+def _ld(t, shape, N, name, what):
+    """Row stride of a row tensor that must have x's shape (None: N)."""
+    if t is None:
+        return N
+    if t.shape != shape:
+        raise ValueError(f"{name}: {what} must have x's shape")
+    return _view(t, N, name, what)[1]
 
 
 def _code(t, name):
@@ -129,36 +179,49 @@ def _code(t, name):
 
 
 def rmsnorm_fwd_rstd(x, gamma, eps, y=None, rstd=None):
-    """Forward that saves rstd ([I769] Scope/tasks item 2). Returns (y, rstd)."""
-    dt = _code(x, "rmsnorm_fwd_rstd")
-    x2 = _rows(x, gamma, "rmsnorm_fwd_rstd")
-    M, N = x2.shape
-    y = torch.empty_like(x) if y is None else y
+    """Forward that saves rstd ([I769] Scope/tasks item 2). Returns (y, rstd).
+    Row tensors may be views with one row stride (the *_strided entry point)."""
+    fn = "rmsnorm_fwd_rstd"
+    dt = _code(x, fn)
+    M, N, ldx = _rows(x, gamma, fn)
+    y = torch.empty(x.shape, dtype=x.dtype, device=x.device) if y is None else y
     rstd = torch.empty(M, dtype=torch.float32, device=x.device) if rstd is None else rstd
-    _same("rmsnorm_fwd_rstd", x, gamma, y)
+    _same(fn, x, gamma, y)
+    ldy = _ld(y, x.shape, N, fn, "y")
     _check_rstd(rstd, M, x.device)
-    st = _on_device(x.device, lambda: lib().rmsnorm_fwd_rstd(
-        _p(x2), _p(gamma), _p(y), _p(rstd), M, N, float(eps), dt, _stream(x.device)))
-    _raise_on("rmsnorm_fwd_rstd", st)
+    if ldx == N and ldy == N:
+        call = lambda: lib().rmsnorm_fwd_rstd(  # noqa: E731
+            _p(x), _p(gamma), _p(y), _p(rstd), M, N, float(eps), dt, _stream(x.device))
+    else:
+        call = lambda: lib().rmsnorm_fwd_rstd_strided(  # noqa: E731
+            _p(x), ldx, _p(gamma), _p(y), ldy, _p(rstd), M, N, float(eps), dt, _stream(x.device))
+    _raise_on(fn, _on_device(x.device, call))
     return y, rstd
 
 
 def fused_add_rmsnorm_fwd_rstd(x, residual, gamma, eps, out=None, residual_out=None, rstd=None):
     """Fused-add forward ([P800] fused-add commit). Returns (out, residual_out, rstd)."""
-    dt = _code(x, "fused_add_rmsnorm_fwd_rstd")
-    x2 = _rows(x, gamma, "fused_add_rmsnorm_fwd_rstd")
-    if residual.shape != x.shape:
-        raise ValueError("fused_add_rmsnorm_fwd_rstd: residual must have x's shape")
-    M, N = x2.shape
-    out = torch.empty_like(x) if out is None else out
-    residual_out = torch.empty_like(x) if residual_out is None else residual_out
+    fn = "fused_add_rmsnorm_fwd_rstd"
+    dt = _code(x, fn)
+    M, N, ldx = _rows(x, gamma, fn)
+    out = torch.empty(x.shape, dtype=x.dtype, device=x.device) if out is None else out
+    residual_out = torch.empty(x.shape, dtype=x.dtype, device=x.device) if residual_out is None \
+        else residual_out
     rstd = torch.empty(M, dtype=torch.float32, device=x.device) if rstd is None else rstd
-    _same("fused_add_rmsnorm_fwd_rstd", x, residual, gamma, out, residual_out)
+    _same(fn, x, residual, gamma, out, residual_out)
+    ldr = _ld(residual, x.shape, N, fn, "residual")
+    ldo = _ld(out, x.shape, N, fn, "out")
+    ldro = _ld(residual_out, x.shape, N, fn, "residual_out")
     _check_rstd(rstd, M, x.device)
-    st = _on_device(x.device, lambda: lib().fused_add_rmsnorm_fwd_rstd(
-        _p(x2), _p(residual), _p(gamma), _p(out), _p(residual_out), _p(rstd), M, N, float(eps),
-        dt, _stream(x.device)))
-    _raise_on("fused_add_rmsnorm_fwd_rstd", st)
+    if ldx == ldr == ldo == ldro == N:
+        call = lambda: lib().fused_add_rmsnorm_fwd_rstd(  # noqa: E731
+            _p(x), _p(residual), _p(gamma), _p(out), _p(residual_out), _p(rstd), M, N, float(eps), dt,
+            _stream(x.device))
+    else:
+        call = lambda: lib().fused_add_rmsnorm_fwd_rstd_strided(  # noqa: E731
+            _p(x), ldx, _p(residual), ldr, _p(gamma), _p(out), ldo, _p(residual_out), ldro, _p(rstd),
+            M, N, float(eps), dt, _stream(x.device))
+    _raise_on(fn, _on_device(x.device, call))
     return out, residual_out, rstd
 
 
@@ -190,31 +253,42 @@ def _check_rstd(rstd, M, device):
 
 def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags):
     dt = _code(x, fn)
-    x2 = _rows(x, gamma, fn)
-    M, N = x2.shape
-    if dy.shape != x.shape or (dres is not None and dres.shape != x.shape):
-        raise ValueError(f"{fn}: dy/dresidual_out must have x's shape")
-    dx = torch.empty_like(x) if dx is None else dx
+    M, N, ldx = _rows(x, gamma, fn)
+    dx = torch.empty(x.shape, dtype=x.dtype, device=x.device) if dx is None else dx
     dgamma_f32 = torch.empty(N, dtype=torch.float32, device=x.device) if dgamma_f32 is None \
         else dgamma_f32
     _same(fn, x, gamma, dy, dres, dx, dgamma)
+    lddy = _ld(dy, x.shape, N, fn, "dy")
+    ldr = _ld(dres, x.shape, N, fn, "dresidual_out")
+    lddx = _ld(dx, x.shape, N, fn, "dx")
     _check_rstd(rstd, M, x.device)
-    if dgamma_f32.dtype != torch.float32 or dgamma_f32.numel() != N:
-        raise ValueError(f"{fn}: dgamma_f32 must be float32 of N elements")
-    if dgamma is not None and dgamma.numel() != N:
-        raise ValueError(f"{fn}: dgamma must have N elements")
+    if dgamma_f32.dtype != torch.float32:
+        raise ValueError(f"{fn}: dgamma_f32 must be float32")
+    _vec(dgamma_f32, N, fn, "dgamma_f32")
+    if dgamma is not None:
+        _vec(dgamma, N, fn, "dgamma")
     need = rmsnorm_bwd_workspace_bytes(M, N, dt, flags)
     if workspace is None:
         workspace = _cached_workspace(x.device, need)
-    if fn == "rmsnorm_bwd":
-        st = _on_device(x.device, lambda: lib().rmsnorm_bwd(
-            _p(x2), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma),
-            _p(workspace), workspace.numel(), M, N, dt, int(flags), _stream(x.device)))
+    ws, wsb, st_ = _p(workspace), workspace.numel(), _stream(x.device)
+    strided = not (ldx == lddy == ldr == lddx == N)
+    if fn == "rmsnorm_bwd" and not strided:
+        call = lambda: lib().rmsnorm_bwd(  # noqa: E731
+            _p(x), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma), ws, wsb, M, N, dt,
+            int(flags), st_)
+    elif fn == "rmsnorm_bwd":
+        call = lambda: lib().rmsnorm_bwd_strided(  # noqa: E731
+            _p(x), ldx, _p(gamma), _p(dy), lddy, _p(rstd), _p(dx), lddx, _p(dgamma_f32), _p(dgamma), ws,
+            wsb, M, N, dt, int(flags), st_)
+    elif not strided:
+        call = lambda: lib().fused_add_rmsnorm_bwd(  # noqa: E731
+            _p(x), _p(gamma), _p(dy), _p(dres), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma), ws, wsb, M,
+            N, dt, int(flags), st_)
     else:
-        st = _on_device(x.device, lambda: lib().fused_add_rmsnorm_bwd(
-            _p(x2), _p(gamma), _p(dy), _p(dres), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma),
-            _p(workspace), workspace.numel(), M, N, dt, int(flags), _stream(x.device)))
-    _raise_on(fn, st)
+        call = lambda: lib().fused_add_rmsnorm_bwd_strided(  # noqa: E731
+            _p(x), ldx, _p(gamma), _p(dy), lddy, _p(dres), ldr, _p(rstd), _p(dx), lddx, _p(dgamma_f32),
+            _p(dgamma), ws, wsb, M, N, dt, int(flags), st_)
+    _raise_on(fn, _on_device(x.device, call))
     return dx, dgamma_f32, dgamma
 
 
@@ -237,19 +311,24 @@ def layernorm_fwd_stats(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     Returns (y, mean, rstd)."""
     fn = "layernorm_fwd_stats"
     dt = _code(x, fn)
-    x2 = _rows(x, gamma, fn)
-    M, N = x2.shape
-    if beta is not None and (beta.dim() != 1 or beta.numel() != N):
-        raise ValueError(f"{fn}: beta must have N={N} elements")
-    y = torch.empty_like(x) if y is None else y
+    M, N, ldx = _rows(x, gamma, fn)
+    if beta is not None:
+        _vec(beta, N, fn, "beta")
+    y = torch.empty(x.shape, dtype=x.dtype, device=x.device) if y is None else y
     mean = torch.empty(M, dtype=torch.float32, device=x.device) if mean is None else mean
     rstd = torch.empty(M, dtype=torch.float32, device=x.device) if rstd is None else rstd
     _same(fn, x, gamma, beta, y)
+    ldy = _ld(y, x.shape, N, fn, "y")
     _check_rstd(mean, M, x.device)
     _check_rstd(rstd, M, x.device)
-    st = _on_device(x.device, lambda: lib().layernorm_fwd_stats(
-        _p(x2), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd), M, N, float(eps), dt, _stream(x.device)))
-    _raise_on(fn, st)
+    if ldx == ldy == N:
+        call = lambda: lib().layernorm_fwd_stats(  # noqa: E731
+            _p(x), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd), M, N, float(eps), dt, _stream(x.device))
+    else:
+        call = lambda: lib().layernorm_fwd_stats_strided(  # noqa: E731
+            _p(x), ldx, _p(gamma), _p(beta), _p(y), ldy, _p(mean), _p(rstd), M, N, float(eps), dt,
+            _stream(x.device))
+    _raise_on(fn, _on_device(x.device, call))
     return y, mean, rstd
 
 
@@ -263,30 +342,36 @@ def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=
     """LayerNorm backward. Returns (dx, dgamma_f32, dbeta_f32, dgamma, dbeta)."""
     fn = "layernorm_bwd"
     dt = _code(x, fn)
-    x2 = _rows(x, gamma, fn)
-    M, N = x2.shape
-    if dy.shape != x.shape:
-        raise ValueError(f"{fn}: dy must have x's shape")
-    dx = torch.empty_like(x) if dx is None else dx
+    M, N, ldx = _rows(x, gamma, fn)
+    dx = torch.empty(x.shape, dtype=x.dtype, device=x.device) if dx is None else dx
     f32 = dict(dtype=torch.float32, device=x.device)
     dgamma_f32 = torch.empty(N, **f32) if dgamma_f32 is None else dgamma_f32
     dbeta_f32 = torch.empty(N, **f32) if dbeta_f32 is None else dbeta_f32
     _same(fn, x, gamma, dy, dx, dgamma, dbeta)
+    lddy = _ld(dy, x.shape, N, fn, "dy")
+    lddx = _ld(dx, x.shape, N, fn, "dx")
     _check_rstd(mean, M, x.device)
     _check_rstd(rstd, M, x.device)
     for name, t in (("dgamma_f32", dgamma_f32), ("dbeta_f32", dbeta_f32)):
-        if t.dtype != torch.float32 or t.numel() != N:
-            raise ValueError(f"{fn}: {name} must be float32 of N elements")
+        if t.dtype != torch.float32:
+            raise ValueError(f"{fn}: {name} must be float32")
+        _vec(t, N, fn, name)
     for name, t in (("dgamma", dgamma), ("dbeta", dbeta)):
-        if t is not None and t.numel() != N:
-            raise ValueError(f"{fn}: {name} must have N elements")
+        if t is not None:
+            _vec(t, N, fn, name)
     need = layernorm_bwd_workspace_bytes(M, N, dt, flags)
     if workspace is None:
         workspace = _cached_workspace(x.device, need)
-    st = _on_device(x.device, lambda: lib().layernorm_bwd(
-        _p(x2), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32), _p(dbeta_f32), _p(dgamma),
-        _p(dbeta), _p(workspace), workspace.numel(), M, N, dt, int(flags), _stream(x.device)))
-    _raise_on(fn, st)
+    ws, wsb, st_ = _p(workspace), workspace.numel(), _stream(x.device)
+    if ldx == lddy == lddx == N:
+        call = lambda: lib().layernorm_bwd(  # noqa: E731
+            _p(x), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32), _p(dbeta_f32),
+            _p(dgamma), _p(dbeta), ws, wsb, M, N, dt, int(flags), st_)
+    else:
+        call = lambda: lib().layernorm_bwd_strided(  # noqa: E731
+            _p(x), ldx, _p(gamma), _p(dy), lddy, _p(mean), _p(rstd), _p(dx), lddx, _p(dgamma_f32),
+            _p(dbeta_f32), _p(dgamma), _p(dbeta), ws, wsb, M, N, dt, int(flags), st_)
+    _raise_on(fn, _on_device(x.device, call))
     return dx, dgamma_f32, dbeta_f32, dgamma, dbeta
 
 

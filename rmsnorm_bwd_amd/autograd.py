@@ -24,8 +24,18 @@ Pages cited, by title:
 """
 import torch
 
-from . import (fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, layernorm_bwd, layernorm_fwd_stats,
-               rmsnorm_bwd, rmsnorm_fwd_rstd)
+from . import (_view, fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, layernorm_bwd,
+               layernorm_fwd_stats, rmsnorm_bwd, rmsnorm_fwd_rstd)
+
+
+def _rows(t):
+    """t itself when the library can read it in place (rows of unit stride
+    under one row stride), else a contiguous copy."""
+    try:
+        _view(t, t.shape[-1], "", "")
+        return t
+    except ValueError:
+        return t.contiguous()
 
 
 def _weight_grad(dgamma_f32, dgamma, weight):
@@ -39,7 +49,7 @@ class RMSNormFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, weight, eps):
-        x = x.contiguous()
+        x = _rows(x)
         weight = weight.contiguous()
         y, rstd = rmsnorm_fwd_rstd(x, weight, eps)
         ctx.save_for_backward(x, weight, rstd)
@@ -49,7 +59,7 @@ class RMSNormFunction(torch.autograd.Function):
     def backward(ctx, dy):
         x, weight, rstd = ctx.saved_tensors
         dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
-        dx, dgamma_f32, dgamma = rmsnorm_bwd(x, weight, dy.contiguous(), rstd, dgamma=dgamma)
+        dx, dgamma_f32, dgamma = rmsnorm_bwd(x, weight, _rows(dy), rstd, dgamma=dgamma)
         return dx, _weight_grad(dgamma_f32, dgamma, weight), None
 
 
@@ -58,8 +68,8 @@ class FusedAddRMSNormFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, residual, weight, eps):
-        x = x.contiguous()
-        residual = residual.contiguous()
+        x = _rows(x)
+        residual = _rows(residual)
         weight = weight.contiguous()
         out, residual_out, rstd = fused_add_rmsnorm_fwd_rstd(x, residual, weight, eps)
         ctx.save_for_backward(residual_out, weight, rstd)
@@ -70,9 +80,9 @@ class FusedAddRMSNormFunction(torch.autograd.Function):
         added, weight, rstd = ctx.saved_tensors
         if dout is None:
             dout = torch.zeros_like(added)
-        dres = None if dresidual_out is None else dresidual_out.contiguous()
+        dres = None if dresidual_out is None else _rows(dresidual_out)
         dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
-        dx, dgamma_f32, dgamma = fused_add_rmsnorm_bwd(added, weight, dout.contiguous(), dres, rstd,
+        dx, dgamma_f32, dgamma = fused_add_rmsnorm_bwd(added, weight, _rows(dout), dres, rstd,
                                                        dgamma=dgamma)
         # x and residual enter only through their sum: one gradient for both
         return dx, dx, _weight_grad(dgamma_f32, dgamma, weight), None
@@ -101,7 +111,7 @@ class LayerNormFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, weight, bias, eps):
-        x = x.contiguous()
+        x = _rows(x)
         weight = weight.contiguous()
         bias = None if bias is None else bias.contiguous()
         y, mean, rstd = layernorm_fwd_stats(x, weight, bias, eps)
@@ -115,7 +125,7 @@ class LayerNormFunction(torch.autograd.Function):
         half = weight.dtype != torch.float32
         dgamma = torch.empty_like(weight) if half else None
         dbeta = torch.empty_like(weight) if half and ctx.has_bias else None
-        dx, dg32, db32, dgamma, dbeta = layernorm_bwd(x, weight, dy.contiguous(), mean, rstd,
+        dx, dg32, db32, dgamma, dbeta = layernorm_bwd(x, weight, _rows(dy), mean, rstd,
                                                       dgamma=dgamma, dbeta=dbeta)
         dbias = None
         if ctx.has_bias:

@@ -44,6 +44,26 @@ int check_flags(unsigned flags) {
     return RMSN_OK;
 }
 
+// Row strides: every row tensor that is present has N <= ld <= RMSN_MAX_LD.
+struct Rows {
+    const void *p;
+    int64_t ld;
+};
+
+int check_strides(int64_t N, std::initializer_list<Rows> rows) {
+    for (const Rows &r : rows)
+        if (r.p && (r.ld < N || r.ld > RMSN_MAX_LD)) return RMSN_ERR_SHAPE;
+    return RMSN_OK;
+}
+
+// The 16-byte vector path needs every row of every row tensor to start on a
+// 16-byte boundary: the base and the row stride in bytes.
+bool rows_vector_ok(std::initializer_list<Rows> rows, int es) {
+    for (const Rows &r : rows)
+        if (r.p && (!aligned(r.p, 16) || (r.ld * es) % 16 != 0)) return false;
+    return true;
+}
+
 bool all_aligned(std::initializer_list<const void *> ptrs, uintptr_t a) {
     for (const void *p : ptrs)
         if (p && !aligned(p, a)) return false;
@@ -96,10 +116,10 @@ size_t workspace_query(int64_t M, int64_t N, int dtype, unsigned flags, int narr
 
 // Backward of RMSNorm (mean == NULL) or LayerNorm (mean != NULL, with
 // dbeta_f32 / dbeta).
-int bwd_common(const void *x, const void *gamma, const void *dy, const void *dres, const float *mean,
-               const float *rstd, void *dx, float *dgamma_f32, void *dgamma, float *dbeta_f32, void *dbeta,
-               void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
-               void *stream, bool layer) {
+int bwd_common(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy, const void *dres,
+               int64_t lddres, const float *mean, const float *rstd, void *dx, int64_t lddx, float *dgamma_f32,
+               void *dgamma, float *dbeta_f32, void *dbeta, void *workspace, size_t workspace_bytes, int64_t M,
+               int64_t N, int dtype, unsigned flags, void *stream, bool layer) {
     if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
     if (int st = check_shape(M, N)) return st;
     if (int st = check_flags(flags)) return st;
@@ -107,11 +127,15 @@ int bwd_common(const void *x, const void *gamma, const void *dy, const void *dre
     if (layer && !dbeta_f32) return RMSN_ERR_NULL;
     if (M > 0 && (!x || !dy || !rstd || !dx)) return RMSN_ERR_NULL;
     if (layer && M > 0 && !mean) return RMSN_ERR_NULL;
+    if (M > 0) {
+        if (int st = check_strides(N, {{x, ldx}, {dy, lddy}, {dres, lddres}, {dx, lddx}})) return st;
+    }
     const int es = esize(dtype);
     if (!all_aligned({x, gamma, dy, dres, dx, dgamma, dbeta}, es) ||
         !all_aligned({rstd, mean, dgamma_f32, dbeta_f32}, 4) || !aligned(workspace, 256))
         return RMSN_ERR_ALIGN;
-    const bool vector_ok = all_aligned({x, gamma, dy, dres, dx}, 16);
+    const bool vector_ok =
+        aligned(gamma, 16) && rows_vector_ok({{x, ldx}, {dy, lddy}, {dres, lddres}, {dx, lddx}}, es);
     RowPlan p;
     if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
     const int64_t grid = rmsn::bwd_blocks(M, N, p);
@@ -140,6 +164,10 @@ int bwd_common(const void *x, const void *gamma, const void *dy, const void *dre
     a.layer = layer;
     a.M = M;
     a.N = (int)N;
+    a.ldx = ldx;
+    a.lddy = lddy;
+    a.lddres = lddres;
+    a.lddx = lddx;
     a.mode = mode;
     hipError_t e = rmsn::launch_bwd(dtype, p, a, (int)grid, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP;
@@ -156,9 +184,9 @@ int64_t fwd_blocks(int64_t M, const RowPlan &p) {
 
 // Forward of RMSNorm (plain or fused-add) or, with `layer`, LayerNorm (beta
 // nullable, mean saved).
-int fwd_common(const void *x, const void *residual, const void *gamma, const void *beta, void *y,
-               void *residual_out, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
-               void *stream, bool fused, bool layer) {
+int fwd_common(const void *x, int64_t ldx, const void *residual, int64_t ldres, const void *gamma,
+               const void *beta, void *y, int64_t ldy, void *residual_out, int64_t ldres_out, float *mean,
+               float *rstd, int64_t M, int64_t N, float eps, int dtype, void *stream, bool fused, bool layer) {
     if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
     if (int st = check_shape(M, N)) return st;
     if (int st = check_eps(eps)) return st;
@@ -166,10 +194,16 @@ int fwd_common(const void *x, const void *residual, const void *gamma, const voi
     if (M > 0 && (!x || !y || !rstd)) return RMSN_ERR_NULL;
     if (fused && M > 0 && (!residual || !residual_out)) return RMSN_ERR_NULL;
     if (layer && M > 0 && !mean) return RMSN_ERR_NULL;
+    if (!fused) residual = residual_out = nullptr;
+    if (M > 0) {
+        if (int st = check_strides(N, {{x, ldx}, {residual, ldres}, {y, ldy}, {residual_out, ldres_out}}))
+            return st;
+    }
     const int es = esize(dtype);
     if (!all_aligned({x, residual, gamma, beta, y, residual_out}, es) || !all_aligned({rstd, mean}, 4))
         return RMSN_ERR_ALIGN;
-    const bool vector_ok = all_aligned({x, residual, gamma, beta, y, residual_out}, 16);
+    const bool vector_ok = all_aligned({gamma, beta}, 16) &&
+                           rows_vector_ok({{x, ldx}, {residual, ldres}, {y, ldy}, {residual_out, ldres_out}}, es);
     RowPlan p;
     if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
     rmsn::FwdArgs a;
@@ -183,6 +217,10 @@ int fwd_common(const void *x, const void *residual, const void *gamma, const voi
     a.rstd = rstd;
     a.M = M;
     a.N = (int)N;
+    a.ldx = ldx;
+    a.ldres = ldres;
+    a.ldy = ldy;
+    a.ldres_out = ldres_out;
     a.eps = eps;
     hipError_t e = rmsn::launch_fwd(dtype, p, a, (int)fwd_blocks(M, p), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP;
@@ -194,15 +232,29 @@ extern "C" {
 
 int rmsnorm_fwd_rstd(const void *x, const void *gamma, void *y, float *rstd, int64_t M, int64_t N, float eps,
                      int dtype, void *stream) {
-    return fwd_common(x, nullptr, gamma, nullptr, y, nullptr, nullptr, rstd, M, N, eps, dtype, stream, false,
-                      false);
+    return fwd_common(x, N, nullptr, N, gamma, nullptr, y, N, nullptr, N, nullptr, rstd, M, N, eps, dtype, stream,
+                      false, false);
+}
+
+int rmsnorm_fwd_rstd_strided(const void *x, int64_t ldx, const void *gamma, void *y, int64_t ldy, float *rstd,
+                             int64_t M, int64_t N, float eps, int dtype, void *stream) {
+    return fwd_common(x, ldx, nullptr, N, gamma, nullptr, y, ldy, nullptr, N, nullptr, rstd, M, N, eps, dtype,
+                      stream, false, false);
 }
 
 int fused_add_rmsnorm_fwd_rstd(const void *x, const void *residual, const void *gamma, void *out,
                                void *residual_out, float *rstd, int64_t M, int64_t N, float eps, int dtype,
                                void *stream) {
-    return fwd_common(x, residual, gamma, nullptr, out, residual_out, nullptr, rstd, M, N, eps, dtype, stream,
-                      true, false);
+    return fwd_common(x, N, residual, N, gamma, nullptr, out, N, residual_out, N, nullptr, rstd, M, N, eps, dtype,
+                      stream, true, false);
+}
+
+int fused_add_rmsnorm_fwd_rstd_strided(const void *x, int64_t ldx, const void *residual, int64_t ldres,
+                                       const void *gamma, void *out, int64_t ldout, void *residual_out,
+                                       int64_t ldres_out, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+                                       void *stream) {
+    return fwd_common(x, ldx, residual, ldres, gamma, nullptr, out, ldout, residual_out, ldres_out, nullptr, rstd,
+                      M, N, eps, dtype, stream, true, false);
 }
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags) {
@@ -212,21 +264,46 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned fla
 int rmsnorm_bwd(const void *x, const void *gamma, const void *dy, const float *rstd, void *dx,
                 float *dgamma_f32, void *dgamma, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int dtype, unsigned flags, void *stream) {
-    return bwd_common(x, gamma, dy, nullptr, nullptr, rstd, dx, dgamma_f32, dgamma, nullptr, nullptr, workspace,
-                      workspace_bytes, M, N, dtype, flags, stream, false);
+    return bwd_common(x, N, gamma, dy, N, nullptr, N, nullptr, rstd, dx, N, dgamma_f32, dgamma, nullptr, nullptr,
+                      workspace, workspace_bytes, M, N, dtype, flags, stream, false);
+}
+
+int rmsnorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy,
+                        const float *rstd, void *dx, int64_t lddx, float *dgamma_f32, void *dgamma,
+                        void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
+                        void *stream) {
+    return bwd_common(x, ldx, gamma, dy, lddy, nullptr, N, nullptr, rstd, dx, lddx, dgamma_f32, dgamma, nullptr,
+                      nullptr, workspace, workspace_bytes, M, N, dtype, flags, stream, false);
 }
 
 int fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *dy, const void *dresidual_out,
                           const float *rstd, void *dx, float *dgamma_f32, void *dgamma, void *workspace,
                           size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
                           void *stream) {
-    return bwd_common(added, gamma, dy, dresidual_out, nullptr, rstd, dx, dgamma_f32, dgamma, nullptr, nullptr,
-                      workspace, workspace_bytes, M, N, dtype, flags, stream, false);
+    return bwd_common(added, N, gamma, dy, N, dresidual_out, N, nullptr, rstd, dx, N, dgamma_f32, dgamma, nullptr,
+                      nullptr, workspace, workspace_bytes, M, N, dtype, flags, stream, false);
+}
+
+int fused_add_rmsnorm_bwd_strided(const void *added, int64_t ldadded, const void *gamma, const void *dy,
+                                  int64_t lddy, const void *dresidual_out, int64_t lddres, const float *rstd,
+                                  void *dx, int64_t lddx, float *dgamma_f32, void *dgamma, void *workspace,
+                                  size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
+                                  void *stream) {
+    return bwd_common(added, ldadded, gamma, dy, lddy, dresidual_out, lddres, nullptr, rstd, dx, lddx, dgamma_f32,
+                      dgamma, nullptr, nullptr, workspace, workspace_bytes, M, N, dtype, flags, stream, false);
 }
 
 int layernorm_fwd_stats(const void *x, const void *gamma, const void *beta, void *y, float *mean, float *rstd,
                         int64_t M, int64_t N, float eps, int dtype, void *stream) {
-    return fwd_common(x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, dtype, stream, false, true);
+    return fwd_common(x, N, nullptr, N, gamma, beta, y, N, nullptr, N, mean, rstd, M, N, eps, dtype, stream, false,
+                      true);
+}
+
+int layernorm_fwd_stats_strided(const void *x, int64_t ldx, const void *gamma, const void *beta, void *y,
+                                int64_t ldy, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+                                void *stream) {
+    return fwd_common(x, ldx, nullptr, N, gamma, beta, y, ldy, nullptr, N, mean, rstd, M, N, eps, dtype, stream,
+                      false, true);
 }
 
 size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned flags) {
@@ -236,8 +313,16 @@ size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, unsigned f
 int layernorm_bwd(const void *x, const void *gamma, const void *dy, const float *mean, const float *rstd,
                   void *dx, float *dgamma_f32, float *dbeta_f32, void *dgamma, void *dbeta, void *workspace,
                   size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags, void *stream) {
-    return bwd_common(x, gamma, dy, nullptr, mean, rstd, dx, dgamma_f32, dgamma, dbeta_f32, dbeta, workspace,
-                      workspace_bytes, M, N, dtype, flags, stream, true);
+    return bwd_common(x, N, gamma, dy, N, nullptr, N, mean, rstd, dx, N, dgamma_f32, dgamma, dbeta_f32, dbeta,
+                      workspace, workspace_bytes, M, N, dtype, flags, stream, true);
+}
+
+int layernorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy,
+                          const float *mean, const float *rstd, void *dx, int64_t lddx, float *dgamma_f32,
+                          float *dbeta_f32, void *dgamma, void *dbeta, void *workspace, size_t workspace_bytes,
+                          int64_t M, int64_t N, int dtype, unsigned flags, void *stream) {
+    return bwd_common(x, ldx, gamma, dy, lddy, nullptr, N, mean, rstd, dx, lddx, dgamma_f32, dgamma, dbeta_f32,
+                      dbeta, workspace, workspace_bytes, M, N, dtype, flags, stream, true);
 }
 
 const char *rmsn_status_string(int status) {

@@ -111,6 +111,17 @@ __device__ __forceinline__ void partial_store(V v, V *p) {
 #endif
 }
 
+// Buffer descriptor for one window of a row tensor with row stride ld
+// elements: rows wb .. wb + nr - 1 exist, and the range ends at the end of the
+// last of them, so rows past M, chunks past N and the gap between strided rows
+// all fall outside it.
+template <int ES>
+__device__ __forceinline__ rsrc_t window_rsrc(const void *base, int64_t wb, int64_t ld, uint32_t nr,
+                                              uint32_t row_bytes) {
+    const uint32_t span = nr == 0 ? 0u : (uint32_t)((int64_t)(nr - 1) * ld * ES) + row_bytes;
+    return make_rsrc(at(base, wb * ld, ES), span);
+}
+
 // The operation a row kernel instance computes.
 enum : int { OP_RMS = 0, OP_RMS_FUSED = 1, OP_LN = 2 };
 
@@ -155,7 +166,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     const int nchunk = N / VEC;
     const int grp = threadIdx.x / TPR;
     const int lt = threadIdx.x % TPR;
-    const uint32_t goff = (uint32_t)grp * row_bytes;
+    // byte offset of the thread's row in a window, per row tensor (zero with
+    // one row a window)
+    const uint32_t gx = (uint32_t)(grp * a.ldx * ES), gd = (uint32_t)(grp * a.lddy * ES);
+    const uint32_t gz = (uint32_t)(grp * a.lddres * ES), gw = (uint32_t)(grp * a.lddx * ES);
 
     // byte offset of each owned chunk inside a row; chunks past the row end
     // get an offset outside every descriptor range
@@ -189,18 +203,18 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     const int64_t w0 = (int64_t)blockIdx.x * RPB;
 
     auto load_window = [&](int64_t wb, P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float &r, float &mu) {
-        const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
-        const rsrc_t rx = make_rsrc(at(a.x, wb * N, ES), bytes);
-        const rsrc_t rd = make_rsrc(at(a.dy, wb * N, ES), bytes);
+        const uint32_t nr = rows_in<RPB>(wb, M);
+        const rsrc_t rx = window_rsrc<ES>(a.x, wb, a.ldx, nr, row_bytes);
+        const rsrc_t rd = window_rsrc<ES>(a.dy, wb, a.lddy, nr, row_bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, goff + coff[k]);
-            dv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, goff + coff[k]);
+            xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, gx + coff[k]);
+            dv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, gd + coff[k]);
         }
         if constexpr (FUSED) {
-            const rsrc_t rz = make_rsrc(at(a.dres, wb * N, ES), bytes);
+            const rsrc_t rz = window_rsrc<ES>(a.dres, wb, a.lddres, nr, row_bytes);
 #pragma unroll
-            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, goff + coff[k]);
+            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, gz + coff[k]);
         }
         const rsrc_t rt = make_rsrc(at(a.rstd, wb, 4), rows_in<RPB>(wb, M) * 4u);
         r = buf_load_f32(rt, (uint32_t)grp * 4u);
@@ -277,10 +291,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         }
     };
     auto store_dx = [&](int64_t wb, const P (&out)[K]) {
-        const rsrc_t rw = make_rsrc(at(a.dx, wb * N, ES), rows_in<RPB>(wb, M) * row_bytes);
+        const rsrc_t rw = window_rsrc<ES>(a.dx, wb, a.lddx, rows_in<RPB>(wb, M), row_bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_DX_STORE>(rw, goff + coff[k], out[k]);
+            buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_DX_STORE>(rw, gw + coff[k], out[k]);
     };
 
     // Block b takes the windows b, b + G, b + 2G, ... (G blocks in the grid).
@@ -521,7 +535,9 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
     const int nchunk = N / VEC;
     const int grp = threadIdx.x / TPR;
     const int lt = threadIdx.x % TPR;
-    const uint32_t goff = (uint32_t)grp * row_bytes;
+    // byte offset of the thread's row in a window, per row tensor
+    const uint32_t gx = (uint32_t)(grp * a.ldx * ES), gr = (uint32_t)(grp * a.ldres * ES);
+    const uint32_t gy = (uint32_t)(grp * a.ldy * ES), go = (uint32_t)(grp * a.ldres_out * ES);
 
     uint32_t coff[K];
 #pragma unroll
@@ -549,14 +565,14 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
     const uint32_t rstd_off = lt == 0 ? (uint32_t)grp * 4u : OOB;
 
     auto load_window = [&](int64_t wb, P (&xv)[K], P (&rv)[FUSED ? K : 1]) {
-        const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
-        const rsrc_t rx = make_rsrc(at(a.x, wb * N, ES), bytes);
+        const uint32_t nr = rows_in<RPB>(wb, M);
+        const rsrc_t rx = window_rsrc<ES>(a.x, wb, a.ldx, nr, row_bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, goff + coff[k]);
+        for (int k = 0; k < K; ++k) xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, gx + coff[k]);
         if constexpr (FUSED) {
-            const rsrc_t rz = make_rsrc(at(a.residual, wb * N, ES), bytes);
+            const rsrc_t rz = window_rsrc<ES>(a.residual, wb, a.ldres, nr, row_bytes);
 #pragma unroll
-            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, goff + coff[k]);
+            for (int k = 0; k < K; ++k) rv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, gr + coff[k]);
         }
     };
 
@@ -629,14 +645,14 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         }
     };
     auto store_rows = [&](int64_t wb, const P (&av)[K], const P (&yo)[K]) {
-        const uint32_t bytes = rows_in<RPB>(wb, M) * row_bytes;
-        const rsrc_t ry = make_rsrc(at(a.y, wb * N, ES), bytes);
+        const uint32_t nr = rows_in<RPB>(wb, M);
+        const rsrc_t ry = window_rsrc<ES>(a.y, wb, a.ldy, nr, row_bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ry, goff + coff[k], yo[k]);
+        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ry, gy + coff[k], yo[k]);
         if constexpr (FUSED) {
-            const rsrc_t ro = make_rsrc(at(a.residual_out, wb * N, ES), bytes);
+            const rsrc_t ro = window_rsrc<ES>(a.residual_out, wb, a.ldres_out, nr, row_bytes);
 #pragma unroll
-            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ro, goff + coff[k], av[k]);
+            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ro, go + coff[k], av[k]);
         }
     };
 

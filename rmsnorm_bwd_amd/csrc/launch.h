@@ -23,6 +23,7 @@ struct BwdArgs {
     void *dbeta;         // (N) in the dtype, or null; LayerNorm only
     int64_t M;
     int N;
+    int64_t ldx, lddy, lddres, lddx;  // row strides in elements (N for contiguous rows)
     int mode;            // DG_DIRECT / DG_PARTIAL / DG_ATOMIC
     bool layer;          // LayerNorm (mean, dbeta) rather than RMSNorm
 };
@@ -38,6 +39,7 @@ struct FwdArgs {
     float *rstd;           // (M)
     int64_t M;
     int N;
+    int64_t ldx, ldres, ldy, ldres_out;  // row strides in elements (N for contiguous rows)
     float eps;
 };
 

@@ -252,3 +252,71 @@ def test_workspace_query():
             for dt in (R.F32, R.F16, R.BF16):
                 v = q(M, N, dt)
                 assert 256 <= v <= 256 + 256 * (-(-N // 16) * 16) * 4
+
+
+# --------------------------------------------------------------------------
+# Strided twins: row strides are validated like shapes
+# --------------------------------------------------------------------------
+
+MAX_LD = 1 << 24
+
+
+def bwd_strided(ldx=64, lddy=64, lddx=64, **kw):
+    a = dict(x=A, gamma=A, dy=A, rstd=A, dx=A, dg32=A, dg=None, ws=A, wsb=0, M=4, N=64,
+             dtype=R.BF16, flags=0)
+    a.update(kw)
+    return R.lib().rmsnorm_bwd_strided(P(a["x"]), ldx, P(a["gamma"]), P(a["dy"]), lddy,
+                                       P(a["rstd"]), P(a["dx"]), lddx, P(a["dg32"]), P(a["dg"]),
+                                       P(a["ws"]), a["wsb"], a["M"], a["N"], a["dtype"],
+                                       a["flags"], None)
+
+
+def fused_bwd_strided(ldx=64, lddy=64, ldres=64, lddx=64, dres=A):
+    return R.lib().fused_add_rmsnorm_bwd_strided(P(A), ldx, P(A), P(A), lddy, P(dres), ldres,
+                                                 P(A), P(A), lddx, P(A), None, P(A), 0, 4, 64,
+                                                 R.BF16, 0, None)
+
+
+def ln_bwd_strided(ldx=64, lddy=64, lddx=64):
+    return R.lib().layernorm_bwd_strided(P(A), ldx, P(A), P(A), lddy, P(A), P(A), P(A), lddx,
+                                         P(A), P(A), None, None, P(A), 0, 4, 64, R.BF16, 0, None)
+
+
+@pytest.mark.parametrize("which", ["ldx", "lddy", "lddx"])
+@pytest.mark.parametrize("ld,want", [(63, SHAPE), (0, SHAPE), (-64, SHAPE), (MAX_LD + 1, SHAPE),
+                                     (64, WORKSPACE), (1000, WORKSPACE), (MAX_LD, WORKSPACE)])
+def test_backward_row_strides(which, ld, want):
+    # a valid stride is accepted and the call then stops at the (too small)
+    # workspace, before any launch
+    assert bwd_strided(**{which: ld}) == want
+    assert ln_bwd_strided(**{which: ld}) == want
+    assert fused_bwd_strided(**{which: ld}) == want
+
+
+def test_fused_backward_dresidual_stride():
+    assert fused_bwd_strided(ldres=10) == SHAPE
+    # a NULL dresidual_out (zeros) has no stride to check
+    assert fused_bwd_strided(ldres=10, dres=None) == WORKSPACE
+
+
+def test_strides_do_not_matter_without_rows():
+    assert bwd_strided(M=0, ldx=1, lddy=1, lddx=1) == WORKSPACE
+    assert R.lib().rmsnorm_fwd_rstd_strided(P(A), 1, P(A), P(A), 1, P(A), 0, 64, 1e-5, R.BF16,
+                                            None) == OK
+
+
+def test_forward_row_strides():
+    fs = R.lib().rmsnorm_fwd_rstd_strided
+    assert fs(P(A), 63, P(A), P(A + 2), 64, P(A), 2, 64, 1e-5, R.BF16, None) == SHAPE
+    assert fs(P(A), 64, P(A), P(A + 2), MAX_LD + 1, P(A), 2, 64, 1e-5, R.BF16, None) == SHAPE
+    # valid strides: stops at the misaligned y, before any launch
+    assert fs(P(A), 100, P(A), P(A + 1), 64, P(A), 2, 64, 1e-5, R.BF16, None) == ALIGN
+    ff = R.lib().fused_add_rmsnorm_fwd_rstd_strided
+    for bad in range(4):
+        ld = [64, 64, 64, 64]
+        ld[bad] = 10
+        assert ff(P(A), ld[0], P(A), ld[1], P(A), P(A + 1), ld[2], P(A), ld[3], P(A), 2, 64, 1e-5,
+                  R.BF16, None) == SHAPE
+    fl = R.lib().layernorm_fwd_stats_strided
+    assert fl(P(A), 10, P(A), None, P(A + 1), 64, P(A), P(A), 2, 64, 1e-5, R.BF16, None) == SHAPE
+    assert fl(P(A), 64, P(A), None, P(A + 1), 64, P(A), P(A), 2, 64, 1e-5, R.BF16, None) == ALIGN
