@@ -147,6 +147,11 @@ __device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
 // that keeps the compiler's memory-counter waits exact, so a window's use
 // never waits on the loads of the windows behind it.
 // ---------------------------------------------------------------------------
+// Pause between the ring's first windows, in units of 64 cycles (s_sleep).
+#ifndef RMSN_PROLOGUE_PAUSE
+#define RMSN_PROLOGUE_PAUSE 8
+#endif
+
 template <int DT, int VEC, int TPR, int K, int BLOCK, int DEPTH, int OP>
 __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
@@ -303,10 +308,16 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     // loads, which would make the memory counter's sequence on entering the
     // loop differ from the one on its back edge; the compiler then merges
     // the two pessimistically and waits for windows a step does not use.
+    // A short pause (512 cycles) after each window but the last lets the
+    // memory system return the first window before the rest, so the first
+    // dx stores start earlier: measured on MI355X, 4096 x 4096 bf16 21.4 ->
+    // 20.9 us and 1024 x 4096 10.3 -> 9.9 us; the fused backward is unchanged,
+    // and longer pauses lose again.
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) {
         load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s], mr[s]);
         asm volatile("" ::: "memory");
+        if (s + 1 < DEPTH) __builtin_amdgcn_s_sleep(RMSN_PROLOGUE_PAUSE);
     }
     int parity = 0;
     // Steady state: groups of DEPTH windows that all hold rows, with no
