@@ -308,16 +308,20 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     // loads, which would make the memory counter's sequence on entering the
     // loop differ from the one on its back edge; the compiler then merges
     // the two pessimistically and waits for windows a step does not use.
-    // A short pause (512 cycles) after each window but the last lets the
-    // memory system return the first window before the rest, so the first
-    // dx stores start earlier: measured on MI355X, 4096 x 4096 bf16 21.4 ->
-    // 20.9 us and 1024 x 4096 10.3 -> 9.9 us; the fused backward is unchanged,
-    // and longer pauses lose again.
+    // When the block's ring fills, a short pause (512 cycles) after each
+    // window but the last lets the memory system return the first window
+    // before the rest, so the first dx stores start earlier: measured on
+    // MI355X, 4096 x 4096 bf16 21.4 -> 20.9-21.2 us and 1024 x 4096 10.3 ->
+    // 9.9 us; the fused backward is unchanged, and longer pauses lose again.
+    // A block with fewer windows (one row: a latency-bound call) does not
+    // pause. The test is made once: a test per window costs 0.25 us at
+    // 4096 x 4096, and two copies of the prologue cost more.
+    const bool full_ring = w0 + (DEPTH - 1) * wstride < M;
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) {
         load_window(w0 + s * wstride, xs[s], ds[s], rs[s], rr[s], mr[s]);
         asm volatile("" ::: "memory");
-        if (s + 1 < DEPTH) __builtin_amdgcn_s_sleep(RMSN_PROLOGUE_PAUSE);
+        if (s + 1 < DEPTH && full_ring) __builtin_amdgcn_s_sleep(RMSN_PROLOGUE_PAUSE);
     }
     int parity = 0;
     // Steady state: groups of DEPTH windows that all hold rows, with no
@@ -667,10 +671,17 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         }
     };
 
+    const bool full_ring = w0 + (DEPTH - 1) * wstride < M;
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) {
         load_window(w0 + s * wstride, xs[s], rs[s]);
         asm volatile("" ::: "memory");  // window order, as in the backward
+        // the backward's prologue pause; measured on MI355X it takes the plain
+        // forward at 4096 x 4096 bf16 from 13.25 to 13.0 us and at 16384 x
+        // 4096 from 42.9 to 42.1 us, and does nothing for the fused forward
+        if constexpr (!FUSED) {
+            if (s + 1 < DEPTH && full_ring) __builtin_amdgcn_s_sleep(RMSN_PROLOGUE_PAUSE);
+        }
     }
     int parity = 0;
     // As in the backward: full groups without branches, and each window's
