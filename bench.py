@@ -256,7 +256,7 @@ def main():
                          "known traffic, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(dgamma would need one all-reduce per step across GPUs).", file=sys.stderr)
         sys.exit(2)
 
