@@ -166,6 +166,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     float *comb = lds + 2 * NA * RPB * WPR;
 
     const int N = a.N;
+    const float inv_n = 1.0f / (float)N;  // one rounding: a multiply, not a divide per row
     const int64_t M = a.M;
     const uint32_t row_bytes = (uint32_t)N * ES;
     const int nchunk = N / VEC;
@@ -239,38 +240,60 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     // r*c2. Every row sum flips `parity`. The window's dx is packed into
     // `out`; the caller issues the next window's loads before the stores (see
     // the loop below).
+    //
+    // A thread whose share of the row is at most 16 values keeps x (centred
+    // for LayerNorm) and wdy from the first pass in fp32 registers for the
+    // second; with a larger share the second pass recomputes them from the
+    // packed row, since keeping 2 * K * VEC fp32 values live across the sum
+    // spills (measured on MI355X: keeping them takes fused 1024 x 8192 bf16
+    // from 19.0 to 18.5 us and leaves 4096 x 4096 unchanged or faster, while at
+    // 32 values a thread 1024 x 16384 goes from 27.4 to 36.7 us).
+    constexpr bool KEEP = K * VEC <= 16;
     auto compute = [&](P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, float mu, int &parity,
                        P (&out)[K]) {
         float b, d = 0.f;
+        float xk[KEEP ? K : 1][KEEP ? VEC : 1], wk[KEEP ? K : 1][KEEP ? VEC : 1];
         if constexpr (LN) {
             float p1 = 0.f, p2 = 0.f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
+                    const float xc = elem(xv[k], e) - mu;
                     const float wd = elem(dv[k], e) * elem(gp[k], e);
-                    p1 = fmaf(elem(xv[k], e) - mu, wd, p1);
+                    if constexpr (KEEP) {
+                        xk[k][e] = xc;
+                        wk[k][e] = wd;
+                    }
+                    p1 = fmaf(xc, wd, p1);
                     p2 += wd;
                 }
             row_sum2<TPR, BLOCK>(p1, p2, slots, parity);
             parity ^= 1;
-            const float c1 = p1 * r / (float)N;
+            const float c1 = p1 * r * inv_n;
             b = r * r * c1;
-            d = r * (p2 / (float)N);
+            d = r * (p2 * inv_n);
         } else {
             float part = 0.f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) part = fmaf(elem(xv[k], e), elem(dv[k], e) * elem(gp[k], e), part);
-            const float c1 = row_sum<TPR, BLOCK>(part, slots, parity) * r / (float)N;
+                for (int e = 0; e < VEC; ++e) {
+                    const float wd = elem(dv[k], e) * elem(gp[k], e);
+                    if constexpr (KEEP) {
+                        xk[k][e] = elem(xv[k], e);
+                        wk[k][e] = wd;
+                    }
+                    part = fmaf(elem(xv[k], e), wd, part);
+                }
+            const float c1 = row_sum<TPR, BLOCK>(part, slots, parity) * r * inv_n;
             parity ^= 1;
             b = r * r * c1;
         }
-        // Recompute from the packed row below instead of keeping 2 * K * VEC
-        // fp32 values live across the sum.
+        if constexpr (!KEEP) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
+            for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
+        }
         // The same for rstd (and the mean). Passing its ring register through
         // an in-place asm also keeps the register allocator from moving the
         // slot's next rstd into a different register, which would need a
@@ -283,9 +306,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             float o[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const float xv_e = LN ? elem(xv[k], e) - mu2 : elem(xv[k], e);
+                const float xv_e = KEEP ? xk[k][e] : (LN ? elem(xv[k], e) - mu2 : elem(xv[k], e));
                 const float dyv = elem(dv[k], e);
-                float dd = fmaf(-b, xv_e, r2 * (dyv * elem(gp[k], e)));
+                const float wd = KEEP ? wk[k][e] : dyv * elem(gp[k], e);
+                float dd = fmaf(-b, xv_e, r2 * wd);
                 if constexpr (LN) dd -= d;
                 if constexpr (FUSED) dd += elem(rv[k], e);
                 o[e] = dd;
