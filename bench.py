@@ -109,6 +109,30 @@ def time_calls(fn, sets, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def time_graph(fn, sets, steps, warmup):
+    """Average ms per call of `steps` calls (cycling through the sets, as
+    time_calls does) captured in one HIP graph and replayed once, after
+    `warmup` eager calls and one untimed replay: the same GPU work without the
+    host's launch overhead between kernels, so kernels run back to back."""
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            fn(sets[i % len(sets)])
+    graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(end) / steps
+
+
 def copy_bandwidth(mib=512, reps=10):
     """Achievable HBM bandwidth on this part: a device-to-device copy of
     `mib` MiB (twice the memory-side cache), read + write bytes per second."""
@@ -251,6 +275,10 @@ def main():
                     help="time the dgamma modes on an (M, N) grid (one JSON line per shape) and exit")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the copy-bandwidth and one-row latency figures (profiled runs)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time every loop as one replay of a HIP graph of the calls (kernels back "
+                         "to back, as a profiler's kernel trace then sees them); value stays "
+                         "the per-call time of that replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device-to-device copy of MIB MiB (a kernel of "
                          "known traffic, to scale hardware byte counters)")
@@ -278,8 +306,12 @@ def main():
     nsets = 1 if args.hot else max(2, -(-ROTATE_BYTES // per_set))
     g, sets = make_sets(w, d, nsets)
     bwd = lambda s: call_bwd(w, g, s)  # noqa: E731
-    ms = time_calls(bwd, sets, args.steps, args.warmup)
-    ms_hot = ms if args.hot else time_calls(bwd, sets[:1], args.steps, args.warmup)
+    timer = time_graph if args.graph else time_calls
+    ms = timer(bwd, sets, args.steps, args.warmup)
+    ms_hot = ms if args.hot else timer(bwd, sets[:1], args.steps, args.warmup)
+    # the other timing method on the same calls, for comparison (skipped in
+    # profiled runs, which trace only the chosen one)
+    ms_other = None if args.no_extras else (time_calls if args.graph else time_graph)(bwd, sets, args.steps, 2)
 
     def fwd(s):
         if w.op == "plain":
@@ -289,7 +321,7 @@ def main():
         else:
             R.fused_add_rmsnorm_fwd_rstd(s["x"], s["dy"], g, w.eps, out=s["dx"],
                                          residual_out=s["dres"], rstd=s["rstd"])
-    ms_fwd = time_calls(fwd, sets, args.steps, args.warmup)
+    ms_fwd = timer(fwd, sets, args.steps, args.warmup)
 
     abytes = algorithmic_bytes(w)
     gbps = abytes / (ms * 1e-3) / 1e9
@@ -314,10 +346,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "dtype": w.dtype,
                    "eps": w.eps, "buffer_sets": nsets,
-                   "timing": "hot" if args.hot else "rotated over > 512 MiB"},
+                   "timing": ("hot" if args.hot else "rotated over > 512 MiB")
+                   + ("; HIP graph replay" if args.graph else "; eager calls")},
         "achieved_GBps": round(gbps, 1),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "hot_cache_us": round(ms_hot * 1e3, 2),
+        ("eager_us" if args.graph else "graph_us"): round(ms_other * 1e3, 2) if ms_other else None,
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "pct_of_copy": round(100 * gbps / copy_gbps, 1) if copy_gbps else None,
         "latency": latency,
