@@ -31,6 +31,9 @@
  *     slower element-wise path with identical results.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *     the null stream). A status of RMSN_OK means the launch was enqueued.
+ *     Only kernels are enqueued (no memset or copy nodes, no allocation),
+ *     so calls may be captured into a HIP graph and replayed; the workspace
+ *     carries no state from one call to the next.
  *   - Arguments are validated before anything is enqueued; a rejected call
  *     writes nothing. Inputs and outputs must not overlap, except where an
  *     entry point says so.
