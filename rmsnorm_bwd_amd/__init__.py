@@ -245,6 +245,24 @@ def _cached_workspace(device, need):
     return ws
 
 
+def _f32_vec(t, N, device, fn, name):
+    """A float32 per-column output (dgamma_f32, dbeta_f32) on x's device."""
+    if t.dtype != torch.float32:
+        raise ValueError(f"{fn}: {name} must be float32")
+    if t.device != device:
+        raise ValueError(f"{fn}: {name} must be on x's device")
+    _vec(t, N, fn, name)
+
+
+def _workspace(workspace, need, device, fn):
+    """(pointer, bytes) of the caller's workspace, or of the cached one."""
+    if workspace is None:
+        workspace = _cached_workspace(device, need)
+    elif workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"{fn}: workspace must be a contiguous tensor on x's device")
+    return _p(workspace), workspace.numel() * workspace.element_size()
+
+
 def _check_rstd(rstd, M, device):
     if rstd.dtype != torch.float32 or rstd.numel() != M or not rstd.is_contiguous() \
             or rstd.device != device:
@@ -262,15 +280,12 @@ def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags)
     ldr = _ld(dres, x.shape, N, fn, "dresidual_out")
     lddx = _ld(dx, x.shape, N, fn, "dx")
     _check_rstd(rstd, M, x.device)
-    if dgamma_f32.dtype != torch.float32:
-        raise ValueError(f"{fn}: dgamma_f32 must be float32")
-    _vec(dgamma_f32, N, fn, "dgamma_f32")
+    _f32_vec(dgamma_f32, N, x.device, fn, "dgamma_f32")
     if dgamma is not None:
         _vec(dgamma, N, fn, "dgamma")
     need = rmsnorm_bwd_workspace_bytes(M, N, dt, flags)
-    if workspace is None:
-        workspace = _cached_workspace(x.device, need)
-    ws, wsb, st_ = _p(workspace), workspace.numel(), _stream(x.device)
+    ws, wsb = _workspace(workspace, need, x.device, fn)
+    st_ = _stream(x.device)
     strided = not (ldx == lddy == ldr == lddx == N)
     if fn == "rmsnorm_bwd" and not strided:
         call = lambda: lib().rmsnorm_bwd(  # noqa: E731
@@ -353,16 +368,13 @@ def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=
     _check_rstd(mean, M, x.device)
     _check_rstd(rstd, M, x.device)
     for name, t in (("dgamma_f32", dgamma_f32), ("dbeta_f32", dbeta_f32)):
-        if t.dtype != torch.float32:
-            raise ValueError(f"{fn}: {name} must be float32")
-        _vec(t, N, fn, name)
+        _f32_vec(t, N, x.device, fn, name)
     for name, t in (("dgamma", dgamma), ("dbeta", dbeta)):
         if t is not None:
             _vec(t, N, fn, name)
     need = layernorm_bwd_workspace_bytes(M, N, dt, flags)
-    if workspace is None:
-        workspace = _cached_workspace(x.device, need)
-    ws, wsb, st_ = _p(workspace), workspace.numel(), _stream(x.device)
+    ws, wsb = _workspace(workspace, need, x.device, fn)
+    st_ = _stream(x.device)
     if ldx == lddy == lddx == N:
         call = lambda: lib().layernorm_bwd(  # noqa: E731
             _p(x), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32), _p(dbeta_f32),

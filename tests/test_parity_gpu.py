@@ -247,3 +247,28 @@ def test_device_check_flag_refuses_host_memory():
     dx2, dg2, _ = R.rmsnorm_bwd(x, g, x, rstd, flags=R.CHECK_DEVICE)
     torch.cuda.synchronize()
     assert torch.isfinite(dx2).all() and torch.isfinite(dg2).all()
+
+
+def test_binding_refuses_host_outputs_and_workspace():
+    """The binding checks, before any launch, that the fp32 weight-gradient
+    outputs and a caller's workspace are on x's device (a host pointer would
+    otherwise reach the kernel)."""
+    N, M = 256, 4
+    x = torch.randn(M, N, device=DEV)
+    g = torch.ones(N, device=DEV)
+    rstd = torch.ones(M, device=DEV)
+    with pytest.raises(ValueError):
+        R.rmsnorm_bwd(x, g, x, rstd, dgamma_f32=torch.empty(N))
+    with pytest.raises(ValueError):
+        R.rmsnorm_bwd(x, g, x, rstd, workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        R.layernorm_bwd(x, g, x, rstd, rstd, dbeta_f32=torch.empty(N))
+    # a float32 workspace is sized in bytes, not elements
+    need = R.rmsnorm_bwd_workspace_bytes(64, 4096, torch.float32)
+    xs = torch.randn(64, 4096, device=DEV)
+    gs = torch.ones(4096, device=DEV)
+    rs = torch.ones(64, device=DEV)
+    ws = torch.zeros((need + 3) // 4, dtype=torch.float32, device=DEV)
+    dx, dg, _ = R.rmsnorm_bwd(xs, gs, xs, rs, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dx).all() and torch.isfinite(dg).all()
