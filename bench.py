@@ -218,8 +218,10 @@ def mode_sweep():
                 torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, d, calls=5):
-    """The CPU oracle (fp64, single thread) on the same workload."""
+def cpu_baseline(w, d, budget_s=10.0, max_calls=200):
+    """The CPU oracle (fp64, single thread) on the same workload: whole calls
+    repeated for about `budget_s` seconds of CPU work (at least three), the
+    median per call reported."""
     import oracle
     x = d["x"] if w.op in ("plain", "layernorm") else None
     if w.op == "plain":
@@ -234,14 +236,14 @@ def cpu_baseline(w, d, calls=5):
         run = lambda: oracle.fused_add_rmsnorm_bwd(added, d["gamma"], d["dy"],  # noqa: E731
                                                    d["dresidual_out"], rstd)
     ts = []
-    for _ in range(calls):
+    while len(ts) < 3 or (sum(ts) < budget_s and len(ts) < max_calls):
         t0 = time.perf_counter()
         run()
         ts.append(time.perf_counter() - t0)
     us = statistics.median(ts) * 1e6
     return {"value": round(us, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {calls} calls, median; "
-                      "fp64 C oracle, one thread",
+            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {len(ts)} calls "
+                      f"({sum(ts):.1f} s of CPU work), median; fp64 C oracle, one thread",
             "GBps": round(algorithmic_bytes(w) / us / 1e3, 2)}
 
 
