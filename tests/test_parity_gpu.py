@@ -272,3 +272,30 @@ def test_binding_refuses_host_outputs_and_workspace():
     dx, dg, _ = R.rmsnorm_bwd(xs, gs, xs, rs, workspace=ws)
     torch.cuda.synchronize()
     assert torch.isfinite(dx).all() and torch.isfinite(dg).all()
+
+
+def test_concurrent_streams_each_get_their_own_workspace():
+    """Backward calls queued on two streams at once (default priority), with
+    no workspace passed: the binding keeps one workspace per stream, so the
+    calls do not share partials; each result is held to the oracle."""
+    _say("case two streams")
+    cases = []
+    for seed, M in ((101, 2048), (102, 1536)):
+        w = workloads.custom("plain", M, 4096, "bf16", 1e-6, seed=seed)
+        d = workloads.make_inputs(w)
+        r, _ = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps, want_y=False)
+        cases.append((w, d, r))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    dev_in = [(d["x"].to(DEV), d["gamma"].to(DEV), d["dy"].to(DEV), r.to(DEV)) for _, d, r in cases]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        outs = []
+        for s, (x, g, dy, r) in zip(streams, dev_in):
+            with torch.cuda.stream(s):
+                outs.append(R.rmsnorm_bwd(x, g, dy, r))
+        torch.cuda.synchronize()
+    for (w, d, r), (dx, dg32, _) in zip(cases, outs):
+        dx_ref, dg_ref = oracle.rmsnorm_bwd(d["x"], d["gamma"], d["dy"], r)
+        assert_close("dx", dx, dx_ref, w.torch_dtype)
+        assert rel(dg32, dg_ref) <= tol_dgamma(w.M)
