@@ -21,8 +21,8 @@
  *
  * Readings taken where the pages leave a step open (each is also listed in the
  * design notes of the repository):
- *   - "cast back to the I/O dtype" is round-to-nearest-even (RNE); a NaN
- *     encodes as a quiet NaN.
+ *   - converting an fp32 result back to the I/O dtype rounds to nearest,
+ *     ties to even (RNE); a NaN encodes as a quiet NaN.
  *   - the fused forward forms added = x + residual as one fp32 addition, then
  *     one RNE to the I/O dtype; rstd is taken over that stored, rounded added,
  *     which is also what the backward reads.
