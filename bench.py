@@ -29,6 +29,7 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 ROTATE_BYTES = 600 << 20  # > 2 x the 256 MiB memory-side cache
+OP_NAMES = {"plain": "rmsnorm_bwd", "fused": "fused_add_rmsnorm_bwd", "layernorm": "layernorm_bwd"}
 
 
 def algorithmic_bytes(w):
@@ -218,6 +219,74 @@ def mode_sweep():
                 torch.cuda.empty_cache()
 
 
+# The shapes of the public-API comparison on [P854] (Benchmark contract, its
+# timing table), with the pages' own MI355X times in microseconds: the
+# FlyDSL backward and torch's, both through autograd.
+API_SHAPES = [
+    # op, M, N, dtype, pages' FlyDSL us, pages' torch us
+    ("plain", 1, 4096, "bf16", 85.4, 42.8), ("fused", 1, 4096, "bf16", 98.6, 83.2),
+    ("plain", 128, 4096, "bf16", 92.2, 57.5), ("fused", 128, 4096, "bf16", 114.5, 76.7),
+    ("plain", 4096, 4096, "bf16", 157.2, 67.7), ("fused", 4096, 4096, "bf16", 160.2, 82.4),
+    ("plain", 512, 2048, "bf16", 81.2, 48.5), ("fused", 512, 2048, "bf16", 100.3, 64.0),
+    ("plain", 512, 3000, "f32", 77.6, 48.6), ("fused", 512, 3000, "f32", 94.8, 63.4),
+    ("plain", 1024, 8192, "bf16", 81.1, 47.5), ("fused", 1024, 8192, "bf16", 102.0, 74.7),
+]
+
+
+def api_compare(warmup=10, iters=100, windows=5):
+    """Backward through the public autograd API, this library's wrappers
+    against torch's eager RMSNorm (torch.nn.functional.rms_norm; for the
+    fused-add form, torch's add then rms_norm), timed the way [P854]'s
+    benchmark contract times them: the forward graph is built before timing;
+    each backward allocates its gradients and includes the weight gradient's
+    reduction and its cast to the parameter dtype; hot cache; HIP events
+    around `iters` backward calls after `warmup`. Both sides are bound by the
+    host (the autograd engine and Python) at most of these shapes, so each
+    figure is the median over `windows` such loops. Gradients of the two are
+    compared before timing. One JSON line per shape."""
+    import torch.nn.functional as F
+    from rmsnorm_bwd_amd.autograd import fused_add_rmsnorm, rmsnorm
+    dev = torch.device("cuda:0")
+    for op, M, N, dt, pages_dsl, pages_torch in API_SHAPES:
+        w = workloads.custom(op, M, N, dt, 1e-6, dy_sigma=1e-2)
+        d = workloads.make_inputs(w)
+
+        def graph(impl):
+            weight = d["gamma"].to(dev).requires_grad_()
+            x = d["x"].to(dev).requires_grad_()
+            dy = d["dy"].to(dev)
+            if op == "plain":
+                y = rmsnorm(x, weight, w.eps) if impl == "ours" else F.rms_norm(x, (N,), weight, w.eps)
+                return (y,), (dy,), (x, weight)
+            res = d["residual"].to(dev).requires_grad_()
+            if impl == "ours":
+                out, res_out = fused_add_rmsnorm(x, res, weight, w.eps)
+            else:
+                res_out = x + res
+                out = F.rms_norm(res_out, (N,), weight, w.eps)
+            return (out, res_out), (dy, d["dresidual_out"].to(dev)), (x, res, weight)
+
+        line = {"api_compare": f"{'rmsnorm_bwd' if op == 'plain' else 'fused_add_bwd'} {M}x{N} {dt}"}
+        grads = {}
+        for impl in ("ours", "torch"):
+            outs, douts, inputs = graph(impl)
+            fn = lambda: torch.autograd.grad(outs, inputs, douts, retain_graph=True)  # noqa: E731
+            grads[impl] = fn()
+            runs = [time_calls(lambda _: fn(), [None], iters, warmup if k == 0 else 0)
+                    for k in range(windows)]
+            line[f"{impl}_us"] = round(statistics.median(runs) * 1e3, 2)
+        g_o, g_t = grads["ours"], grads["torch"]
+
+        def rdiff(a, b):
+            a, b = a.double(), b.double()
+            return float((a - b).abs().max() / b.abs().max().clamp_min(1e-30))
+        line["dx_rel_diff"] = rdiff(g_o[0], g_t[0])
+        line["dweight_rel_diff"] = rdiff(g_o[-1], g_t[-1])
+        line["pages_flydsl_us"] = pages_dsl
+        line["pages_torch_us"] = pages_torch
+        print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(w, d, budget_s=10.0, max_calls=200):
     """The CPU oracle (fp64, single thread) on the same workload: whole calls
     repeated for about `budget_s` seconds of CPU work (at least three), the
@@ -275,6 +344,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--mode-sweep", action="store_true",
                     help="time the dgamma modes on an (M, N) grid (one JSON line per shape) and exit")
+    ap.add_argument("--api-compare", action="store_true",
+                    help="time the backward through autograd against torch's eager RMSNorm on the "
+                         "pages' public-API shapes (one JSON line per shape) and exit")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the copy-bandwidth and one-row latency figures (profiled runs)")
     ap.add_argument("--graph", action="store_true",
@@ -292,6 +364,9 @@ def main():
 
     if args.mode_sweep:
         mode_sweep()
+        return
+    if args.api_compare:
+        api_compare()
         return
 
     if args.copy_calibration:
@@ -334,7 +409,8 @@ def main():
     latency = None if skip else latency_floor()
     line = {
         "metric": "rmsnorm_bwd us/call + achieved HBM GB/s (% of peak), 4096x4096 bf16"
-                  if w.op != "layernorm" else f"layernorm_bwd us/call + achieved HBM GB/s, {w.name}",
+                  if w.name == workloads.HEADLINE
+                  else f"{OP_NAMES[w.op]} us/call + achieved HBM GB/s (% of peak), {w.M}x{w.N} {w.dtype}",
         "value": round(ms * 1e3, 2),
         "unit": "us/call",
         "n_gpus": 1,

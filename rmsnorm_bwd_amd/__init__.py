@@ -93,17 +93,39 @@ def _raise_on(fn, status):
 
 
 def _p(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # an int (or None for NULL): ctypes converts it through the declared
+    # c_void_p argument type
+    return None if t is None else t.data_ptr()
+
+
+# torch's raw accessors of the current stream and device when it has them:
+# the same values as torch.cuda.current_stream(d).cuda_stream and
+# torch.cuda.current_device(), without building Python objects on every call
+_raw_stream_fn = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_raw_device_fn = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _raw_stream(device):
+    """The current HIP stream of `device`, as an integer handle."""
+    if _raw_stream_fn is not None:
+        return _raw_stream_fn(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _cur_dev():
+    if _raw_device_fn is not None and torch.cuda.is_initialized():
+        return _raw_device_fn()
+    return torch.cuda.current_device()
 
 
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return _raw_stream(device)
 
 
 def _on_device(device, fn, *args):
     """Call fn with `device` current (the library launches on the current
     device, as the pages' device guard requires), switching only if needed."""
-    if device.index == torch.cuda.current_device():
+    if device.index == _cur_dev():
         return fn(*args)
     with torch.cuda.device(device):
         return fn(*args)
@@ -122,13 +144,15 @@ def _view(t, N, name, what):
     of wider rows). Anything else is refused; the caller can copy it."""
     if t.dim() == 0 or t.shape[-1] != N:
         raise ValueError(f"{name}: {what} must have rows of N={N} elements")
+    if t.is_contiguous():
+        return t.numel() // N, N
     if N > 1 and t.stride(-1) != 1:
         raise ValueError(f"{name}: {what} must have unit stride along its rows")
     lead = [(sz, st) for sz, st in zip(t.shape[:-1], t.stride()[:-1]) if sz != 1]
     M = 1
     for sz, _ in lead:
         M *= sz
-    if not lead or t.is_contiguous():
+    if not lead:
         return M, N
     for (sz, st), (sz2, st2) in zip(lead[:-1], lead[1:]):
         if st != st2 * sz2:
@@ -151,19 +175,27 @@ def _rows(x, gamma, name):
     return M, N, ld
 
 
+def _didx(device):
+    """A device's index as Tensor.get_device() gives it (-1 off the GPU)."""
+    return -1 if device.index is None or device.type != "cuda" else device.index
+
+
 def _same(name, ref, *ts):
+    dtype, dev = ref.dtype, ref.get_device()  # device index (-1 on the host)
     for t in ts:
         if t is None:
             continue
-        if t.dtype != ref.dtype:
-            raise TypeError(f"{name}: dtype mismatch {t.dtype} vs {ref.dtype}")
-        if t.device != ref.device:
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: dtype mismatch {t.dtype} vs {dtype}")
+        if t.get_device() != dev:
             raise ValueError(f"{name}: tensors on different devices")
 
 
 def _ld(t, shape, N, name, what):
     """Row stride of a row tensor that must have x's shape (None: N)."""
     if t is None:
+        return N
+    if t.is_contiguous() and t.shape == shape:
         return N
     if t.shape != shape:
         raise ValueError(f"{name}: {what} must have x's shape")
@@ -225,9 +257,23 @@ def fused_add_rmsnorm_fwd_rstd(x, residual, gamma, eps, out=None, residual_out=N
     return out, residual_out, rstd
 
 
-def rmsnorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
+_ws_bytes = {}
+
+
+def _ws_query(entry, M, N, dtype, flags):
+    """The library's workspace answer, remembered per arguments (it depends
+    on nothing else)."""
     code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
-    return int(lib().rmsnorm_bwd_workspace_bytes(int(M), int(N), code, int(flags)))
+    key = (entry, M, N, code, flags)
+    b = _ws_bytes.get(key)
+    if b is None:
+        b = int(getattr(lib(), entry)(int(M), int(N), code, int(flags)))
+        _ws_bytes[key] = b
+    return b
+
+
+def rmsnorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
+    return _ws_query("rmsnorm_bwd_workspace_bytes", M, N, dtype, flags)
 
 
 # One workspace per (device, stream), reused by calls that pass none: calls on
@@ -236,8 +282,8 @@ def rmsnorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
 _workspaces = {}
 
 
-def _cached_workspace(device, need):
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+def _cached_workspace(device, need, stream):
+    key = (device.index, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
@@ -249,43 +295,44 @@ def _f32_vec(t, N, device, fn, name):
     """A float32 per-column output (dgamma_f32, dbeta_f32) on x's device."""
     if t.dtype != torch.float32:
         raise ValueError(f"{fn}: {name} must be float32")
-    if t.device != device:
+    if t.get_device() != _didx(device):
         raise ValueError(f"{fn}: {name} must be on x's device")
     _vec(t, N, fn, name)
 
 
-def _workspace(workspace, need, device, fn):
+def _workspace(workspace, need, device, fn, stream):
     """(pointer, bytes) of the caller's workspace, or of the cached one."""
     if workspace is None:
-        workspace = _cached_workspace(device, need)
-    elif workspace.device != device or not workspace.is_contiguous():
+        workspace = _cached_workspace(device, need, stream)
+    elif workspace.get_device() != _didx(device) or not workspace.is_contiguous():
         raise ValueError(f"{fn}: workspace must be a contiguous tensor on x's device")
     return _p(workspace), workspace.numel() * workspace.element_size()
 
 
 def _check_rstd(rstd, M, device):
     if rstd.dtype != torch.float32 or rstd.numel() != M or not rstd.is_contiguous() \
-            or rstd.device != device:
+            or rstd.get_device() != _didx(device):
         raise ValueError("rstd must be a contiguous float32 tensor of M elements on x's device")
 
 
 def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags):
     dt = _code(x, fn)
     M, N, ldx = _rows(x, gamma, fn)
-    dx = torch.empty(x.shape, dtype=x.dtype, device=x.device) if dx is None else dx
-    dgamma_f32 = torch.empty(N, dtype=torch.float32, device=x.device) if dgamma_f32 is None \
+    dev, shape = x.device, x.shape
+    dx = torch.empty(shape, dtype=x.dtype, device=dev) if dx is None else dx
+    dgamma_f32 = torch.empty(N, dtype=torch.float32, device=dev) if dgamma_f32 is None \
         else dgamma_f32
     _same(fn, x, gamma, dy, dres, dx, dgamma)
-    lddy = _ld(dy, x.shape, N, fn, "dy")
-    ldr = _ld(dres, x.shape, N, fn, "dresidual_out")
-    lddx = _ld(dx, x.shape, N, fn, "dx")
-    _check_rstd(rstd, M, x.device)
-    _f32_vec(dgamma_f32, N, x.device, fn, "dgamma_f32")
+    lddy = _ld(dy, shape, N, fn, "dy")
+    ldr = _ld(dres, shape, N, fn, "dresidual_out")
+    lddx = _ld(dx, shape, N, fn, "dx")
+    _check_rstd(rstd, M, dev)
+    _f32_vec(dgamma_f32, N, dev, fn, "dgamma_f32")
     if dgamma is not None:
         _vec(dgamma, N, fn, "dgamma")
     need = rmsnorm_bwd_workspace_bytes(M, N, dt, flags)
-    ws, wsb = _workspace(workspace, need, x.device, fn)
-    st_ = _stream(x.device)
+    st_ = _stream(dev)
+    ws, wsb = _workspace(workspace, need, dev, fn, st_)
     strided = not (ldx == lddy == ldr == lddx == N)
     if fn == "rmsnorm_bwd" and not strided:
         call = lambda: lib().rmsnorm_bwd(  # noqa: E731
@@ -303,7 +350,7 @@ def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags)
         call = lambda: lib().fused_add_rmsnorm_bwd_strided(  # noqa: E731
             _p(x), ldx, _p(gamma), _p(dy), lddy, _p(dres), ldr, _p(rstd), _p(dx), lddx, _p(dgamma_f32),
             _p(dgamma), ws, wsb, M, N, dt, int(flags), st_)
-    _raise_on(fn, _on_device(x.device, call))
+    _raise_on(fn, _on_device(dev, call))
     return dx, dgamma_f32, dgamma
 
 
@@ -348,8 +395,7 @@ def layernorm_fwd_stats(x, gamma, beta, eps, y=None, mean=None, rstd=None):
 
 
 def layernorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
-    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
-    return int(lib().layernorm_bwd_workspace_bytes(int(M), int(N), code, int(flags)))
+    return _ws_query("layernorm_bwd_workspace_bytes", M, N, dtype, flags)
 
 
 def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=None, dgamma=None,
@@ -373,8 +419,8 @@ def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=
         if t is not None:
             _vec(t, N, fn, name)
     need = layernorm_bwd_workspace_bytes(M, N, dt, flags)
-    ws, wsb = _workspace(workspace, need, x.device, fn)
     st_ = _stream(x.device)
+    ws, wsb = _workspace(workspace, need, x.device, fn, st_)
     if ldx == lddy == lddx == N:
         call = lambda: lib().layernorm_bwd(  # noqa: E731
             _p(x), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32), _p(dbeta_f32),

@@ -31,6 +31,8 @@ from . import (_view, fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, layerno
 def _rows(t):
     """t itself when the library can read it in place (rows of unit stride
     under one row stride), else a contiguous copy."""
+    if t.is_contiguous():
+        return t
     try:
         _view(t, t.shape[-1], "", "")
         return t
