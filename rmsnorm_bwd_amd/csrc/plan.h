@@ -36,6 +36,7 @@ inline int pow2_ceil(int64_t v) {
 //   RMSN_K_MIN           fewest 16-byte chunks per thread on the vector path
 //   RMSN_DEPTH           most row windows in flight per row group
 //   RMSN_RING_VGPRS      registers per thread the window ring may take
+//   RMSN_FIN_TILE        columns per tile of the dgamma partials (16, 32 or 64)
 #ifndef RMSN_BWD_MAX_BLOCKS
 #define RMSN_BWD_MAX_BLOCKS 256
 #endif
@@ -139,7 +140,11 @@ enum : int { DG_DIRECT = 0, DG_PARTIAL = 1, DG_ATOMIC = 2 };
 // holds, for every block g, the block's partials of columns
 // [FIN_TILE t, FIN_TILE (t + 1)) contiguously, so one tile is a [G][FIN_TILE]
 // array and the finalize reads it in one contiguous run.
-constexpr int FIN_TILE = 16;
+#ifndef RMSN_FIN_TILE
+#define RMSN_FIN_TILE 16
+#endif
+constexpr int FIN_TILE = RMSN_FIN_TILE;
+static_assert(FIN_TILE == 16 || FIN_TILE == 32 || FIN_TILE == 64, "partial tile of 16, 32 or 64 columns");
 
 constexpr int64_t partial_index(int64_t col, int64_t block, int64_t G) {
     return (col / FIN_TILE) * G * FIN_TILE + block * FIN_TILE + col % FIN_TILE;
