@@ -24,8 +24,8 @@ Pages cited, by title:
 """
 import torch
 
-from . import (_view, fused_add_rmsnorm_bwd, fused_add_rmsnorm_fwd_rstd, layernorm_bwd,
-               layernorm_fwd_stats, rmsnorm_bwd, rmsnorm_fwd_rstd)
+from . import (_bwd_saved, _view, fused_add_rmsnorm_fwd_rstd, layernorm_bwd, layernorm_fwd_stats,
+               rmsnorm_fwd_rstd)
 
 
 def _rows(t):
@@ -61,7 +61,7 @@ class RMSNormFunction(torch.autograd.Function):
     def backward(ctx, dy):
         x, weight, rstd = ctx.saved_tensors
         dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
-        dx, dgamma_f32, dgamma = rmsnorm_bwd(x, weight, _rows(dy), rstd, dgamma=dgamma)
+        dx, dgamma_f32, dgamma = _bwd_saved("rmsnorm_bwd", x, weight, _rows(dy), None, rstd, dgamma)
         return dx, _weight_grad(dgamma_f32, dgamma, weight), None
 
 
@@ -84,8 +84,8 @@ class FusedAddRMSNormFunction(torch.autograd.Function):
             dout = torch.zeros_like(added)
         dres = None if dresidual_out is None else _rows(dresidual_out)
         dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
-        dx, dgamma_f32, dgamma = fused_add_rmsnorm_bwd(added, weight, _rows(dout), dres, rstd,
-                                                       dgamma=dgamma)
+        dx, dgamma_f32, dgamma = _bwd_saved("fused_add_rmsnorm_bwd", added, weight, _rows(dout), dres,
+                                            rstd, dgamma)
         # x and residual enter only through their sum: one gradient for both
         return dx, dx, _weight_grad(dgamma_f32, dgamma, weight), None
 
