@@ -76,7 +76,12 @@ typedef enum {
  *                              inputs give the same bits on every call;
  *   RMSN_DGAMMA_ATOMIC         partials are added with fp32 atomics into
  *                              dgamma_f32; the sum order, so the last bits of
- *                              dgamma, may vary from call to call.
+ *                              dgamma, may vary from call to call. These are
+ *                              the hardware fp32 adds of device memory:
+ *                              dgamma_f32 (and dbeta_f32) must be ordinary
+ *                              device allocations (hipMalloc), not host,
+ *                              managed or fine-grained memory, where such
+ *                              adds do not take effect.
  * RMSN_CHECK_DEVICE additionally checks, with the HIP runtime, that every
  * pointer belongs to the current device (the fault the pages' device guard
  * fixed: [P800] review-fix commit). */
@@ -149,7 +154,6 @@ int fused_add_rmsnorm_bwd(const void *added, const void *gamma, const void *dy,
                           void *workspace, size_t workspace_bytes,
                           int64_t M, int64_t N, int dtype, unsigned flags, void *stream);
 
-/* A static, human-readable name for a status code. */
 /* LayerNorm forward that saves its statistics. [I769] PR sequence and status
  * updates: the LayerNorm follow-up's forward saves mean and rstd (fp32), with
  * weight and bias length checks. Taken as the textbook layer norm:
@@ -210,6 +214,7 @@ int layernorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const v
                           void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
                           unsigned flags, void *stream);
 
+/* A static, human-readable name for a status code. */
 const char *rmsn_status_string(int status);
 
 #ifdef __cplusplus
