@@ -1,0 +1,89 @@
+// Exercises the host-side launch planning (rmsnorm_bwd_amd/csrc/plan.h) over
+// every row length the library accepts, both element sizes and both load
+// paths, and a range of row counts up to the largest M, checking the
+// invariants the kernels rely on. Built with AddressSanitizer and
+// UndefinedBehaviorSanitizer by tests/test_host_sanitizers.py, so signed
+// overflow in the size arithmetic is reported too. Exit status 0 when every
+// invariant holds.
+#include <cstdint>
+#include <cstdio>
+#include <initializer_list>
+
+#include "plan.h"
+
+using namespace rmsn;
+
+static int failures = 0;
+#define CHECK(c, ...)                                   \
+    do {                                                \
+        if (!(c)) {                                     \
+            if (failures++ < 20) {                      \
+                std::fprintf(stderr, "%s: ", #c);       \
+                std::fprintf(stderr, __VA_ARGS__);      \
+                std::fprintf(stderr, "\n");             \
+            }                                           \
+        }                                               \
+    } while (0)
+
+static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int main() {
+    RowPlan p;
+    CHECK(!plan_rows(0, 2, true, &p), "N = 0 accepted");
+    CHECK(!plan_rows(MAX_N + 1, 2, true, &p), "N = MAX_N + 1 accepted");
+    const int64_t Ms[] = {0, 1, 2, 15, 16, 17, 255, 256, 257, 4095, 4096, 32768, 1000003, (int64_t(1) << 31) - 1};
+    for (int esize : {2, 4}) {
+        for (int vok = 0; vok < 2; ++vok) {
+            for (int64_t N = 1; N <= MAX_N; ++N) {
+                if (!plan_rows(N, esize, vok != 0, &p)) {
+                    CHECK(false, "N = %lld refused", (long long)N);
+                    continue;
+                }
+                const bool vec = p.vec != 1;
+                CHECK(!vec || (vok && p.vec * esize == 16 && N % p.vec == 0), "vector plan for N = %lld", (long long)N);
+                CHECK((int64_t)p.vec * p.k * p.tpr >= N, "plan does not cover N = %lld", (long long)N);
+                CHECK(pow2(p.tpr) && p.tpr >= 16 && p.tpr <= 512, "tpr %d", p.tpr);
+                CHECK(pow2(p.k) && p.k * p.vec <= 32, "k %d vec %d at N = %lld", p.k, p.vec, (long long)N);
+                CHECK(p.block <= 512 && p.block % p.tpr == 0 && p.rpb == p.block / p.tpr, "block %d", p.block);
+                CHECK(p.block % 64 == 0, "block %d not whole wavefronts", p.block);
+                if (N % 97 != 1 && N > 64) continue;  // the row-count sweep on a sample of N
+                for (int64_t M : Ms) {
+                    const int64_t G = bwd_blocks(M, N, p);
+                    CHECK(G >= 1 && G <= BWD_MAX_BLOCKS, "G %lld at M %lld N %lld", (long long)G, (long long)M,
+                          (long long)N);
+                    if (M > 0 && G > 1)
+                        CHECK(G <= (M + p.rpb - 1) / p.rpb, "idle blocks at M %lld", (long long)M);
+                    for (int mode : {DG_DIRECT, DG_PARTIAL, DG_ATOMIC})
+                        for (int na : {1, 2}) {
+                            const size_t ws = bwd_workspace(M, N, p, mode, na);
+                            CHECK(ws >= WS_HEADER, "workspace below its header");
+                            if (mode != DG_PARTIAL) continue;
+                            // the last partial of every array lies inside the workspace
+                            const int64_t tiles = (N + FIN_TILE - 1) / FIN_TILE;
+                            const int64_t pstride = tiles * FIN_TILE * G;
+                            const int64_t last = (na - 1) * pstride + partial_index(N - 1, G - 1, G);
+                            CHECK((size_t)(last + 1) * sizeof(float) + WS_HEADER <= ws,
+                                  "partial index %lld past a workspace of %zu bytes", (long long)last, ws);
+                            // the header bound the C header states for the default tile
+                            CHECK(ws <= WS_HEADER + (size_t)na * BWD_MAX_BLOCKS * (size_t)(tiles * FIN_TILE) * 4,
+                                  "workspace above its bound");
+                        }
+                }
+            }
+        }
+    }
+    // partial_index is a bijection from (column, block) onto [0, tiles * FIN_TILE * G)
+    for (int64_t G : {int64_t(1), int64_t(2), int64_t(255), int64_t(256)}) {
+        const int64_t N = 100, tiles = (N + FIN_TILE - 1) / FIN_TILE;
+        static unsigned char seen[256 * 112];
+        for (int64_t i = 0; i < tiles * FIN_TILE * G; ++i) seen[i] = 0;
+        for (int64_t b = 0; b < G; ++b)
+            for (int64_t c = 0; c < tiles * FIN_TILE; ++c) {
+                const int64_t k = partial_index(c, b, G);
+                CHECK(k >= 0 && k < tiles * FIN_TILE * G && !seen[k], "partial_index collision");
+                if (k >= 0 && k < tiles * FIN_TILE * G) seen[k] = 1;
+            }
+    }
+    std::printf("plan driver: %d failed checks\n", failures);
+    return failures ? 1 : 0;
+}
