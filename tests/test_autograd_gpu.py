@@ -97,3 +97,39 @@ def test_fused_add_autograd(prenorm):
     assert torch.equal(xg.grad, rg.grad), "x and residual must get one gradient"
     assert_close("dx", xg.grad.reshape(-1, N), dx_ref, torch.bfloat16)
     assert_close("dweight", wg.grad, dg_ref, torch.bfloat16)
+
+
+def test_rmsnorm_autograd_of_a_sum_takes_an_expanded_gradient():
+    """loss = y.sum(): autograd hands the backward a stride-0 (expanded)
+    gradient of ones, which the wrapper must copy before the library reads it."""
+    print("case autograd rmsnorm sum() (5, 768) bf16", flush=True)
+    M, N, eps = 5, 768, 1e-6
+    x = _draw((M, N), 12)
+    w = _draw((N,), 13, 1.0, 0.1)
+    xg = x.to(DEV).requires_grad_()
+    wg = w.to(DEV).requires_grad_()
+    R.rmsnorm(xg, wg, eps).sum().backward()
+    torch.cuda.synchronize()
+    ones = torch.ones(M, N, dtype=torch.bfloat16)
+    r_ref, _ = oracle.rmsnorm_fwd(x, w, eps)
+    dx_ref, dg_ref = oracle.rmsnorm_bwd(x, w, ones, r_ref)
+    assert_close("dx", xg.grad, dx_ref, torch.bfloat16)
+    assert_close("dweight", wg.grad, dg_ref, torch.bfloat16)
+
+
+def test_fused_add_autograd_with_only_residual_out_in_the_loss():
+    """Only residual_out feeds the loss, so the gradient of out arrives as
+    None (zeros): dx must equal the incoming residual gradient exactly, and
+    dweight must be zero."""
+    print("case autograd fused_add_rmsnorm residual_out only (6, 512) bf16", flush=True)
+    M, N, eps = 6, 512, 1e-6
+    x, res = _draw((M, N), 14), _draw((M, N), 15)
+    w = _draw((N,), 16, 1.0, 0.1)
+    g2 = _draw((M, N), 17, 0.0, 1e-2)
+    xg, rg, wg = (t.to(DEV).requires_grad_() for t in (x, res, w))
+    _, res_out = R.fused_add_rmsnorm(xg, rg, wg, eps, prenorm=True)
+    res_out.backward(g2.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(xg.grad.cpu(), g2)
+    assert torch.equal(rg.grad.cpu(), g2)
+    assert torch.count_nonzero(wg.grad).item() == 0
