@@ -19,6 +19,7 @@ Pages cited, by title:
 """
 import ctypes
 import os
+from collections import OrderedDict
 
 import torch
 
@@ -258,6 +259,7 @@ def fused_add_rmsnorm_fwd_rstd(x, residual, gamma, eps, out=None, residual_out=N
 
 
 _ws_bytes = {}
+_WS_BYTES_MAX = 4096  # remembered answers; forgotten all at once past this many
 
 
 def _ws_query(entry, M, N, dtype, flags):
@@ -268,6 +270,8 @@ def _ws_query(entry, M, N, dtype, flags):
     b = _ws_bytes.get(key)
     if b is None:
         b = int(getattr(lib(), entry)(int(M), int(N), code, int(flags)))
+        if len(_ws_bytes) >= _WS_BYTES_MAX:
+            _ws_bytes.clear()
         _ws_bytes[key] = b
     return b
 
@@ -278,8 +282,14 @@ def rmsnorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
 
 # One workspace per (device, stream), reused by calls that pass none: calls on
 # one stream run in order, so they never share it concurrently, and a call
-# then allocates nothing.
-_workspaces = {}
+# then allocates nothing. At most _WS_STREAMS streams keep one, the least
+# recently used giving its up first (a program that creates streams per step
+# would otherwise keep a workspace for every stream it ever used). Dropping
+# one is safe while work that uses it is still queued: torch's caching
+# allocator hands a freed block only to later allocations on the stream that
+# allocated it, which run after that work.
+_workspaces = OrderedDict()
+_WS_STREAMS = 16
 
 
 def _cached_workspace(device, need, stream):
@@ -288,6 +298,9 @@ def _cached_workspace(device, need, stream):
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
+    _workspaces.move_to_end(key)
+    while len(_workspaces) > _WS_STREAMS:
+        _workspaces.popitem(last=False)
     return ws
 
 

@@ -61,3 +61,19 @@ def test_device_index_rule():
     assert R._didx(torch.device("cuda", 0)) == 0
     assert R._didx(torch.device("cuda", 3)) == 3
     assert torch.zeros(1).get_device() == R._didx(torch.zeros(1).device)
+
+
+def test_workspace_cache_keeps_the_most_recent_streams():
+    R._workspaces.clear()
+    cpu = torch.device("cpu")
+    first = R._cached_workspace(cpu, 1000, 1)
+    assert first.numel() >= 1000
+    assert R._cached_workspace(cpu, 500, 1) is first          # reused when large enough
+    bigger = R._cached_workspace(cpu, 5000, 1)
+    assert bigger is not first and bigger.numel() >= 5000     # grown when not
+    for s in range(2, 2 + 2 * R._WS_STREAMS):
+        R._cached_workspace(cpu, 256, s)
+    assert len(R._workspaces) == R._WS_STREAMS
+    assert (None, 1) not in R._workspaces                     # the oldest stream gave its up
+    assert (None, 1 + 2 * R._WS_STREAMS) in R._workspaces
+    R._workspaces.clear()
