@@ -19,6 +19,7 @@ Pages cited, by title:
 """
 import ctypes
 import os
+import threading
 from collections import OrderedDict
 
 import torch
@@ -292,16 +293,20 @@ _workspaces = OrderedDict()
 _WS_STREAMS = 16
 
 
+_workspaces_lock = threading.Lock()  # torch runs backward passes on per-device threads
+
+
 def _cached_workspace(device, need, stream):
     key = (device.index, stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
-    _workspaces.move_to_end(key)
-    while len(_workspaces) > _WS_STREAMS:
-        _workspaces.popitem(last=False)
-    return ws
+    with _workspaces_lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+        _workspaces.move_to_end(key)
+        while len(_workspaces) > _WS_STREAMS:
+            _workspaces.popitem(last=False)
+        return ws
 
 
 def _f32_vec(t, N, device, fn, name):
