@@ -108,6 +108,23 @@ def test_plain_edge_shapes(M, N, dt):
     check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-5, seed=M + N)))
 
 
+# Short rows at large M: each block holds thousands of row windows and folds
+# every one of their rows into its dgamma registers; M is not a multiple of
+# the rows a window holds, so the last window is ragged.
+MANY_ROWS = [(262147, 64, "bf16"), (100003, 256, "f32"), (32771, 1024, "f16")]
+
+
+@pytest.mark.parametrize("M,N,dt", MANY_ROWS)
+def test_plain_short_rows_at_large_M(M, N, dt):
+    _say("case plain many rows", M, N, dt)
+    check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-5, seed=M + N)))
+
+
+def test_fused_short_rows_at_large_M():
+    _say("case fused many rows 131075 128 bf16")
+    check_case(fused_case(workloads.custom("fused", 131075, 128, "bf16", 1e-6, seed=7)))
+
+
 @pytest.mark.parametrize("M,N,dt", EDGE[::2])
 def test_fused_edge_shapes(M, N, dt):
     _say("case fused", M, N, dt)
