@@ -125,6 +125,33 @@ def test_fused_short_rows_at_large_M():
     check_case(fused_case(workloads.custom("fused", 131075, 128, "bf16", 1e-6, seed=7)))
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [40, -40])
+@pytest.mark.parametrize("M,N", [(64, 4096), (7, 3001)])
+def test_extreme_magnitudes(M, N, dt, k):
+    """x scaled by 2^k, which is exact in binary, with eps = 0. The kernel
+    forms dx as r*wdy - (r*r*c1)*x, whose per-row factor r*r is then 2^(-2k)
+    times its usual size; dx and y must keep their accuracy against the oracle
+    on the scaled input."""
+    _say("case magnitude 2^%d" % k, M, N, dt)
+    w = workloads.custom("plain", M, N, dt, 0.0, seed=k & 0xFF)
+    d = workloads.make_inputs(w)
+    T = w.torch_dtype
+    x = (d["x"].double() * 2.0 ** k).to(T)
+    assert torch.equal(x.double() / 2.0 ** k, d["x"].double())  # the scaling was exact
+    r_ref, y_ref = oracle.rmsnorm_fwd(x, d["gamma"], 0.0)
+    xg, gg, dyg = place(x), place(d["gamma"]), place(d["dy"])
+    y, rstd = R.rmsnorm_fwd_rstd(xg, gg, 0.0)
+    dx, dg32, _ = R.rmsnorm_bwd(xg, gg, dyg, r_ref.to(DEV))
+    torch.cuda.synchronize()
+    er = ((rstd.cpu().double() - r_ref.double()).abs() / r_ref.double()).max().item()
+    assert er <= 1e-5
+    assert_close("y", y, y_ref, T)
+    dx_ref, dg_ref = oracle.rmsnorm_bwd(x, d["gamma"], d["dy"], r_ref)
+    assert_close("dx", dx, dx_ref, T)
+    assert rel(dg32, dg_ref) <= tol_dgamma(M)
+
+
 @pytest.mark.parametrize("M,N,dt", EDGE[::2])
 def test_fused_edge_shapes(M, N, dt):
     _say("case fused", M, N, dt)
