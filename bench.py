@@ -420,7 +420,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        # the arithmetic type: every sum, product and reduction is fp32; the
+        # rows are stored in config.dtype
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "dtype": w.dtype,
                    "eps": w.eps, "buffer_sets": nsets,
