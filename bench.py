@@ -219,6 +219,53 @@ def mode_sweep():
                 torch.cuda.empty_cache()
 
 
+def shape_sweep(steps=50):
+    """The backward and the forward of plain and fused-add RMSNorm (bf16) over
+    an (M, N) grid: GPU time per call from one HIP-graph replay of `steps`
+    calls rotating over buffer sets of > 512 MiB (as the headline is timed),
+    algorithmic GB/s and its share of 8 TB/s. One JSON line per shape."""
+    dev = torch.device("cuda:0")
+    for op in ("plain", "fused"):
+        for N in (1024, 2048, 4096, 8192):
+            for M in (1, 128, 512, 1024, 4096, 16384, 32768):
+                w = workloads.custom(op, M, N, "bf16", 1e-6, dy_sigma=1e-2)
+                per = (4 if op == "fused" else 3) * M * N * 2
+                # a replay touches at most `steps` sets; below 512 MiB in all
+                # (short shapes) the calls find their rows in the memory-side
+                # cache, as a latency-bound call of that size would in use
+                nsets = max(2, min(steps, -(-ROTATE_BYTES // per)))
+                g = (1 + 0.1 * torch.randn(N, device=dev)).to(torch.bfloat16)
+                sets = []
+                for _ in range(nsets):
+                    x = torch.randn(M, N, device=dev).to(torch.bfloat16)
+                    _, rstd = R.rmsnorm_fwd_rstd(x, g, w.eps)
+                    t = dict(x=x, dy=(1e-2 * torch.randn(M, N, device=dev)).to(torch.bfloat16),
+                             dres=(1e-2 * torch.randn(M, N, device=dev)).to(torch.bfloat16)
+                             if op == "fused" else None,
+                             rstd=rstd, dx=torch.empty_like(x), dg32=torch.empty(N, device=dev),
+                             dg=torch.empty_like(g))
+                    t["ws"] = torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(M, N, torch.bfloat16)),
+                                          dtype=torch.uint8, device=dev)
+                    sets.append(t)
+
+                def fwd(t):
+                    if op == "plain":
+                        R.rmsnorm_fwd_rstd(t["x"], g, w.eps, y=t["dx"], rstd=t["rstd"])
+                    else:
+                        R.fused_add_rmsnorm_fwd_rstd(t["x"], t["dy"], g, w.eps, out=t["dx"],
+                                                     residual_out=t["dres"], rstd=t["rstd"])
+                us = time_graph(lambda t: call_bwd(w, g, t), sets, steps, 5) * 1e3
+                us_f = time_graph(fwd, sets, steps, 5) * 1e3
+                b, bf = algorithmic_bytes(w), fwd_bytes(w)
+                print(json.dumps({"op": op, "M": M, "N": N, "dtype": "bf16", "bwd_us": round(us, 2),
+                                  "bwd_GBps": round(b / us / 1e3, 1),
+                                  "bwd_pct_of_8TBps": round(100 * b / us / 1e3 / HBM_PEAK_GBPS, 1),
+                                  "fwd_us": round(us_f, 2), "fwd_GBps": round(bf / us_f / 1e3, 1)}),
+                      flush=True)
+                del sets
+                torch.cuda.empty_cache()
+
+
 # The shapes of the public-API comparison on [P854] (Benchmark contract, its
 # timing table), with the pages' own MI355X times in microseconds: the
 # FlyDSL backward and torch's, both through autograd.
@@ -344,6 +391,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--mode-sweep", action="store_true",
                     help="time the dgamma modes on an (M, N) grid (one JSON line per shape) and exit")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="time plain and fused backward and forward (bf16) on an (M, N) grid "
+                         "(one JSON line per shape) and exit")
     ap.add_argument("--api-compare", action="store_true",
                     help="time the backward through autograd against torch's eager RMSNorm on the "
                          "pages' public-API shapes (one JSON line per shape) and exit")
@@ -367,6 +417,9 @@ def main():
         return
     if args.api_compare:
         api_compare()
+        return
+    if args.shape_sweep:
+        shape_sweep()
         return
 
     if args.copy_calibration:
