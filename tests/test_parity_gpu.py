@@ -165,6 +165,31 @@ def test_misaligned_pointers_take_the_element_path(M, N, dt):
     check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-5), misalign=True))
 
 
+@pytest.mark.parametrize("M,N,dt", [(1, 4096, "bf16"), (8, 1024, "bf16"), (32, 256, "bf16"),
+                                     (1, 3000, "f32"), (8, 256, "f16")])
+def test_one_block_call_with_unaligned_gradient_outputs(M, N, dt):
+    """A call whose rows fit one block writes dgamma itself, four columns a
+    store when its outputs allow; outputs that are only element-aligned take
+    element stores and must hold the same bits."""
+    _say("case one block, unaligned dgamma outputs", M, N, dt)
+    w = workloads.custom("plain", M, N, dt, 1e-5, seed=N)
+    d = workloads.make_inputs(w)
+    T = w.torch_dtype
+    x, g, dy = place(d["x"]), place(d["gamma"]), place(d["dy"])
+    r_ref, _ = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps)
+    rstd = r_ref.to(DEV)
+    _, dg32_a, dgt_a = R.rmsnorm_bwd(x, g, dy, rstd, dgamma=torch.empty(N, dtype=T, device=DEV))
+    f32buf = torch.empty(N + 1, dtype=torch.float32, device=DEV)
+    tbuf = torch.empty(N + 1, dtype=T, device=DEV)
+    _, dg32_u, dgt_u = R.rmsnorm_bwd(x, g, dy, rstd, dgamma_f32=f32buf[1:], dgamma=tbuf[1:])
+    torch.cuda.synchronize()
+    assert f32buf[1:].data_ptr() % 16 != 0
+    assert torch.equal(dg32_u.cpu(), dg32_a.cpu()) and torch.equal(dgt_u.cpu(), dgt_a.cpu())
+    assert torch.equal(dgt_u.cpu(), dg32_u.cpu().to(T))
+    _, dg_ref = oracle.rmsnorm_bwd(d["x"], d["gamma"], d["dy"], r_ref)
+    assert rel(dg32_u, dg_ref) <= tol_dgamma(M)
+
+
 @pytest.mark.parametrize("with_dres", [False, True])
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_fused_with_and_without_dresidual(with_dres, dt):
