@@ -360,7 +360,20 @@ def cpu_baseline(w, d, budget_s=10.0, max_calls=200):
     return {"value": round(us, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
             "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {len(ts)} calls "
                       f"({sum(ts):.1f} s of CPU work), median; fp64 C oracle, one thread",
-            "GBps": round(algorithmic_bytes(w) / us / 1e3, 2)}
+            "GBps": round(algorithmic_bytes(w) / us / 1e3, 2),
+            "host": {"cpu_model": _cpu_model(), "logical_cpus": os.cpu_count()}}
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def load_traffic(w):
