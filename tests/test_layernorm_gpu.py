@@ -55,9 +55,13 @@ def _inputs(M, N, dt, seed=31, with_beta=True):
     return x, g, b, dy
 
 
-def run_case(M, N, dt, eps, flags=R.DGAMMA_AUTO, misalign=False, with_beta=True, seed=31):
+def run_case(M, N, dt, eps, flags=R.DGAMMA_AUTO, misalign=False, with_beta=True, seed=31, scale_exp=0):
     x, g, b, dy = _inputs(M, N, dt, seed, with_beta)
     td = T[dt]
+    if scale_exp:
+        xs = (x.double() * 2.0 ** scale_exp).to(td)
+        assert torch.equal(xs.double() / 2.0 ** scale_exp, x.double())  # exact scaling
+        x = xs
     mean_ref, rstd_ref, y_ref = oracle.layernorm_fwd(x, g, b, eps)
     dx_ref, dg_ref, db_ref = oracle.layernorm_bwd(x, g, dy, mean_ref, rstd_ref)
     xg, gg, dyg = place(x, misalign), place(g, misalign), place(dy, misalign)
@@ -174,3 +178,13 @@ def test_layer_norm_autograd_against_oracle_and_fp64_torch():
     assert rel(xa.grad.cpu(), x64.grad) <= 1e-5
     assert rel(wa.grad.cpu(), w64.grad) <= tol_dgamma(24)
     assert rel(ba.grad.cpu(), b64.grad) <= tol_dgamma(24)
+
+
+@pytest.mark.parametrize("k", [40, -40])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_layernorm_extreme_magnitudes(k, dt):
+    """x (mean 0.5) scaled by 2^k, exact in binary, with eps = 0: the mean and
+    the centred values sit 2^k from their usual size and rstd 2^-k; every
+    output must keep its accuracy against the oracle on the scaled input."""
+    print("case layernorm magnitude 2^%d" % k, dt, flush=True)
+    check(run_case(48, 2048, dt, 0.0, seed=53, scale_exp=k))

@@ -152,6 +152,31 @@ def test_extreme_magnitudes(M, N, dt, k):
     assert rel(dg32, dg_ref) <= tol_dgamma(M)
 
 
+@pytest.mark.parametrize("k", [40, -40])
+def test_fused_extreme_magnitudes(k):
+    """x and residual scaled by 2^k (exact in binary), eps = 0: their sum,
+    rounded once, is the unscaled sum times 2^k, and the backward (with a
+    dresidual_out) must keep its accuracy against the oracle."""
+    _say("case fused magnitude 2^%d" % k)
+    M, N = 64, 4096
+    w = workloads.custom("fused", M, N, "bf16", 0.0, seed=k & 0xFF)
+    d = workloads.make_inputs(w)
+    T = w.torch_dtype
+    xs, rs = ((d[n].double() * 2.0 ** k).to(T) for n in ("x", "residual"))
+    a_ref, r_ref, o_ref = oracle.fused_add_rmsnorm_fwd(xs, rs, d["gamma"], 0.0)
+    out, res_out, rstd = R.fused_add_rmsnorm_fwd_rstd(place(xs), place(rs), place(d["gamma"]), 0.0)
+    dx, dg32, _ = R.fused_add_rmsnorm_bwd(place(a_ref), place(d["gamma"]), place(d["dy"]),
+                                          place(d["dresidual_out"]), r_ref.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(res_out.cpu(), a_ref)
+    er = ((rstd.cpu().double() - r_ref.double()).abs() / r_ref.double()).max().item()
+    assert er <= 1e-5
+    assert_close("out", out, o_ref, T)
+    dx_ref, dg_ref = oracle.fused_add_rmsnorm_bwd(a_ref, d["gamma"], d["dy"], d["dresidual_out"], r_ref)
+    assert_close("dx", dx, dx_ref, T)
+    assert rel(dg32, dg_ref) <= tol_dgamma(M)
+
+
 @pytest.mark.parametrize("M,N,dt", EDGE[::2])
 def test_fused_edge_shapes(M, N, dt):
     _say("case fused", M, N, dt)
