@@ -138,7 +138,7 @@ int bwd_common(const void *x, int64_t ldx, const void *gamma, const void *dy, in
         aligned(gamma, 16) && rows_vector_ok({{x, ldx}, {dy, lddy}, {dres, lddres}, {dx, lddx}}, es);
     RowPlan p;
     if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
-    const int64_t grid = rmsn::bwd_blocks(M, N, p);
+    const int64_t grid = rmsn::bwd_blocks(M, N, p, !layer && dres != nullptr);
     const int mode = resolve_mode(flags, grid);
     // the public query's answer, whatever plan the pointers select, so a
     // buffer sized by the query is always accepted and nothing less is

@@ -116,6 +116,13 @@ inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
 // Upper bound on the backward's persistent grid: the number of per-block
 // fp32 dgamma partials the workspace must hold.
 constexpr int BWD_MAX_BLOCKS = RMSN_BWD_MAX_BLOCKS;
+#ifndef RMSN_FUSED_MAX_BLOCKS
+#define RMSN_FUSED_MAX_BLOCKS 192
+#endif
+#ifndef RMSN_FUSED_CAP_MIN_M
+#define RMSN_FUSED_CAP_MIN_M 4096
+#endif
+static_assert(RMSN_FUSED_MAX_BLOCKS <= RMSN_BWD_MAX_BLOCKS, "the workspace query assumes the larger grid");
 constexpr size_t WS_HEADER = 256;
 
 // Blocks the backward launches for M rows: one block per rpb rows at small M,
@@ -126,11 +133,20 @@ constexpr size_t WS_HEADER = 256;
 // 32 x 256 bf16 and 4.2 instead of 5.6 us at 8 x 1024, while one block
 // holding several long rows is latency-bound (64 x 4096 bf16: 39.6 us against
 // 5.4 us with 64 blocks and partials).
-inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p) {
+//
+// A fused-add backward with a dresidual_out reads three row tensors; from
+// 4096 rows on it runs at most 192 blocks (RMSN_FUSED_MAX_BLOCKS,
+// RMSN_FUSED_CAP_MIN_M). Measured on MI355X, bf16, against 256 blocks:
+// 32768 x 8192 354-359 -> 344.5 us, 32768 x 4096 179.3 -> 171.4 us,
+// 8192 x 4096 48.6 -> 46.8 us, 4096 x 4096 27.6 -> 27.0 us; the plain and
+// LayerNorm backwards (two row reads) lose with fewer blocks, and so do
+// fused calls of fewer rows (1024 x 8192: 18.1 -> 19.4 us).
+inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool three_reads = false) {
     if (M <= 0 || (N <= 1024 && M * N <= 8192)) return 1;
     int64_t steps = (M + p.rpb - 1) / p.rpb;
     if (steps < 1) steps = 1;
-    return steps < BWD_MAX_BLOCKS ? steps : BWD_MAX_BLOCKS;
+    const int64_t cap = three_reads && M >= RMSN_FUSED_CAP_MIN_M ? RMSN_FUSED_MAX_BLOCKS : BWD_MAX_BLOCKS;
+    return steps < cap ? steps : cap;
 }
 
 // dgamma combining modes actually run.

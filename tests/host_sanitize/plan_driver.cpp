@@ -53,6 +53,10 @@ int main() {
                           (long long)N);
                     if (M > 0 && G > 1)
                         CHECK(G <= (M + p.rpb - 1) / p.rpb, "idle blocks at M %lld", (long long)M);
+                    // a three-read (fused) call never runs more blocks than the
+                    // workspace query sizes for
+                    const int64_t G3 = bwd_blocks(M, N, p, true);
+                    CHECK(G3 >= 1 && G3 <= G, "fused grid %lld above %lld", (long long)G3, (long long)G);
                     for (int mode : {DG_DIRECT, DG_PARTIAL, DG_ATOMIC})
                         for (int na : {1, 2}) {
                             const size_t ws = bwd_workspace(M, N, p, mode, na);
