@@ -333,7 +333,38 @@ def _check_rstd(rstd, M, device):
         raise ValueError("rstd must be a contiguous float32 tensor of M elements on x's device")
 
 
-def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags):
+class BoundCall:
+    """One backward call checked and marshalled once, for repeated launches
+    over fixed buffers (a training step's static tensors, a timing loop).
+    Calling it enqueues the same entry point with the same pointers on the
+    device's stream that is current at that moment (so the call can also be
+    captured into a HIP graph) and returns the output tensors. It keeps the
+    tensors it was bound to alive; their storage must not be replaced (in-place
+    writes to their values are what a loop does). Calls of one bound object on
+    different streams must not overlap: they share its workspace."""
+
+    __slots__ = ("_name", "_fn", "_args", "_dev", "outputs", "_keep")
+
+    def __init__(self, name, fn, args, dev, outputs, keep):
+        self._name, self._fn, self._args, self._dev = name, fn, args, dev
+        self.outputs, self._keep = outputs, keep
+
+    def __call__(self):
+        _raise_on(self._name, _on_device(self._dev, self._fn, *self._args, _raw_stream(self._dev)))
+        return self.outputs
+
+
+def _bound_workspace(workspace, need, dev, fn):
+    """The workspace a bound call owns: the caller's (checked for size now),
+    or a new one of the size the library asks for."""
+    if workspace is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise RmsnError(fn, 5, "workspace missing or too small")
+    return workspace
+
+
+def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags, bind=False):
     dt = _code(x, fn)
     M, N, ldx = _rows(x, gamma, fn)
     dev, shape = x.device, x.shape
@@ -349,26 +380,29 @@ def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags)
     if dgamma is not None:
         _vec(dgamma, N, fn, "dgamma")
     need = rmsnorm_bwd_workspace_bytes(M, N, dt, flags)
-    st_ = _stream(dev)
+    st_ = None if bind else _stream(dev)
+    if bind:
+        workspace = _bound_workspace(workspace, need, dev, fn)
     ws, wsb = _workspace(workspace, need, dev, fn, st_)
     strided = not (ldx == lddy == ldr == lddx == N)
     if fn == "rmsnorm_bwd" and not strided:
-        call = lambda: lib().rmsnorm_bwd(  # noqa: E731
-            _p(x), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma), ws, wsb, M, N, dt,
-            int(flags), st_)
+        entry, args = "rmsnorm_bwd", (_p(x), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32),
+                                      _p(dgamma), ws, wsb, M, N, dt, int(flags))
     elif fn == "rmsnorm_bwd":
-        call = lambda: lib().rmsnorm_bwd_strided(  # noqa: E731
-            _p(x), ldx, _p(gamma), _p(dy), lddy, _p(rstd), _p(dx), lddx, _p(dgamma_f32), _p(dgamma), ws,
-            wsb, M, N, dt, int(flags), st_)
+        entry, args = "rmsnorm_bwd_strided", (_p(x), ldx, _p(gamma), _p(dy), lddy, _p(rstd), _p(dx), lddx,
+                                              _p(dgamma_f32), _p(dgamma), ws, wsb, M, N, dt, int(flags))
     elif not strided:
-        call = lambda: lib().fused_add_rmsnorm_bwd(  # noqa: E731
-            _p(x), _p(gamma), _p(dy), _p(dres), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma), ws, wsb, M,
-            N, dt, int(flags), st_)
+        entry, args = "fused_add_rmsnorm_bwd", (_p(x), _p(gamma), _p(dy), _p(dres), _p(rstd), _p(dx),
+                                                _p(dgamma_f32), _p(dgamma), ws, wsb, M, N, dt, int(flags))
     else:
-        call = lambda: lib().fused_add_rmsnorm_bwd_strided(  # noqa: E731
+        entry, args = "fused_add_rmsnorm_bwd_strided", (
             _p(x), ldx, _p(gamma), _p(dy), lddy, _p(dres), ldr, _p(rstd), _p(dx), lddx, _p(dgamma_f32),
-            _p(dgamma), ws, wsb, M, N, dt, int(flags), st_)
-    _raise_on(fn, _on_device(dev, call))
+            _p(dgamma), ws, wsb, M, N, dt, int(flags))
+    f = getattr(lib(), entry)
+    if bind:
+        return BoundCall(fn, f, args, dev, (dx, dgamma_f32, dgamma),
+                         (x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace))
+    _raise_on(fn, _on_device(dev, f, *args, st_))
     return dx, dgamma_f32, dgamma
 
 
@@ -416,6 +450,21 @@ def fused_add_rmsnorm_bwd(added, gamma, dy, dresidual_out, rstd, dx=None, dgamma
                 dgamma, workspace, flags)
 
 
+def bind_rmsnorm_bwd(x, gamma, dy, rstd, dx=None, dgamma_f32=None, dgamma=None, workspace=None,
+                     flags=DGAMMA_AUTO):
+    """rmsnorm_bwd's checks and marshalling done once: returns a BoundCall
+    whose call enqueues the backward and returns (dx, dgamma_f32, dgamma)."""
+    return _bwd("rmsnorm_bwd", x, gamma, dy, None, rstd, dx, dgamma_f32, dgamma, workspace, flags,
+                bind=True)
+
+
+def bind_fused_add_rmsnorm_bwd(added, gamma, dy, dresidual_out, rstd, dx=None, dgamma_f32=None,
+                               dgamma=None, workspace=None, flags=DGAMMA_AUTO):
+    """fused_add_rmsnorm_bwd bound once (see bind_rmsnorm_bwd)."""
+    return _bwd("fused_add_rmsnorm_bwd", added, gamma, dy, dresidual_out, rstd, dx, dgamma_f32, dgamma,
+                workspace, flags, bind=True)
+
+
 def layernorm_fwd_stats(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     """LayerNorm forward that saves mean and rstd. beta may be None (zeros).
     Returns (y, mean, rstd)."""
@@ -446,39 +495,58 @@ def layernorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
     return _ws_query("layernorm_bwd_workspace_bytes", M, N, dtype, flags)
 
 
-def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=None, dgamma=None,
-                  dbeta=None, workspace=None, flags=DGAMMA_AUTO):
-    """LayerNorm backward. Returns (dx, dgamma_f32, dbeta_f32, dgamma, dbeta)."""
+def _ln_bwd(x, gamma, dy, mean, rstd, dx, dgamma_f32, dbeta_f32, dgamma, dbeta, workspace, flags, bind):
     fn = "layernorm_bwd"
     dt = _code(x, fn)
     M, N, ldx = _rows(x, gamma, fn)
-    dx = torch.empty(x.shape, dtype=x.dtype, device=x.device) if dx is None else dx
-    f32 = dict(dtype=torch.float32, device=x.device)
+    dev = x.device
+    dx = torch.empty(x.shape, dtype=x.dtype, device=dev) if dx is None else dx
+    f32 = dict(dtype=torch.float32, device=dev)
     dgamma_f32 = torch.empty(N, **f32) if dgamma_f32 is None else dgamma_f32
     dbeta_f32 = torch.empty(N, **f32) if dbeta_f32 is None else dbeta_f32
     _same(fn, x, gamma, dy, dx, dgamma, dbeta)
     lddy = _ld(dy, x.shape, N, fn, "dy")
     lddx = _ld(dx, x.shape, N, fn, "dx")
-    _check_rstd(mean, M, x.device)
-    _check_rstd(rstd, M, x.device)
+    _check_rstd(mean, M, dev)
+    _check_rstd(rstd, M, dev)
     for name, t in (("dgamma_f32", dgamma_f32), ("dbeta_f32", dbeta_f32)):
-        _f32_vec(t, N, x.device, fn, name)
+        _f32_vec(t, N, dev, fn, name)
     for name, t in (("dgamma", dgamma), ("dbeta", dbeta)):
         if t is not None:
             _vec(t, N, fn, name)
     need = layernorm_bwd_workspace_bytes(M, N, dt, flags)
-    st_ = _stream(x.device)
-    ws, wsb = _workspace(workspace, need, x.device, fn, st_)
+    st_ = None if bind else _stream(dev)
+    if bind:
+        workspace = _bound_workspace(workspace, need, dev, fn)
+    ws, wsb = _workspace(workspace, need, dev, fn, st_)
     if ldx == lddy == lddx == N:
-        call = lambda: lib().layernorm_bwd(  # noqa: E731
-            _p(x), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32), _p(dbeta_f32),
-            _p(dgamma), _p(dbeta), ws, wsb, M, N, dt, int(flags), st_)
+        entry, args = "layernorm_bwd", (_p(x), _p(gamma), _p(dy), _p(mean), _p(rstd), _p(dx), _p(dgamma_f32),
+                                        _p(dbeta_f32), _p(dgamma), _p(dbeta), ws, wsb, M, N, dt, int(flags))
     else:
-        call = lambda: lib().layernorm_bwd_strided(  # noqa: E731
+        entry, args = "layernorm_bwd_strided", (
             _p(x), ldx, _p(gamma), _p(dy), lddy, _p(mean), _p(rstd), _p(dx), lddx, _p(dgamma_f32),
-            _p(dbeta_f32), _p(dgamma), _p(dbeta), ws, wsb, M, N, dt, int(flags), st_)
-    _raise_on(fn, _on_device(x.device, call))
-    return dx, dgamma_f32, dbeta_f32, dgamma, dbeta
+            _p(dbeta_f32), _p(dgamma), _p(dbeta), ws, wsb, M, N, dt, int(flags))
+    f = getattr(lib(), entry)
+    outs = (dx, dgamma_f32, dbeta_f32, dgamma, dbeta)
+    if bind:
+        return BoundCall(fn, f, args, dev, outs, (x, gamma, dy, mean, rstd, *outs, workspace))
+    _raise_on(fn, _on_device(dev, f, *args, st_))
+    return outs
+
+
+def layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=None, dgamma=None,
+                  dbeta=None, workspace=None, flags=DGAMMA_AUTO):
+    """LayerNorm backward. Returns (dx, dgamma_f32, dbeta_f32, dgamma, dbeta)."""
+    return _ln_bwd(x, gamma, dy, mean, rstd, dx, dgamma_f32, dbeta_f32, dgamma, dbeta, workspace, flags,
+                   bind=False)
+
+
+def bind_layernorm_bwd(x, gamma, dy, mean, rstd, dx=None, dgamma_f32=None, dbeta_f32=None, dgamma=None,
+                       dbeta=None, workspace=None, flags=DGAMMA_AUTO):
+    """layernorm_bwd bound once (see bind_rmsnorm_bwd); a call returns
+    (dx, dgamma_f32, dbeta_f32, dgamma, dbeta)."""
+    return _ln_bwd(x, gamma, dy, mean, rstd, dx, dgamma_f32, dbeta_f32, dgamma, dbeta, workspace, flags,
+                   bind=True)
 
 
 from .autograd import (FusedAddRMSNormFunction, LayerNormFunction, RMSNormFunction,  # noqa: E402,F401
