@@ -10,6 +10,10 @@ against the oracle's unrounded fp64 result):
 Half-precision dx/y are also held, element by element, within one unit in the
 last place of the dtype plus 1e-5 of the tensor's scale: one rounding of an
 fp32 result whose own error is far below an ulp.
+
+dgamma_f32 is also held column by column to the error bound of an fp32 sum
+(see sum_bound): the normwise 1e-4*sqrt(M) alone would let one row's
+contribution go missing at large M, the bound does not.
 """
 import math
 
@@ -36,6 +40,41 @@ def rel(got, ref):
 
 def tol_dgamma(M):
     return 1e-4 * math.sqrt(max(M, 1))
+
+
+def sum_depth(M):
+    """Upper bound on the fp32 additions any one row's dgamma term passes
+    through in the library: its row group's running sum (rows of a group,
+    at most M with one block, at most ceil(M / 128) once the grid holds 128
+    or more blocks, which every call of more than 8192 rows does), then the
+    fold of at most 16 row groups and the sum over at most 256 block
+    partials (in a fixed order, or by atomics in any order), plus the two
+    roundings of forming the term."""
+    per_group = M if M <= 8192 else -(-M // 128)
+    return per_group + 16 + 256 + 2
+
+
+def sum_bound(abs_sum, M):
+    """Per-column bound on |fp32 sum - exact sum| for M terms of absolute sum
+    abs_sum: first-order error analysis of summation, depth * 2^-24 *
+    sum |t|, with a quarter's margin for second-order terms."""
+    return 1.25 * sum_depth(M) * 2.0 ** -24 * abs_sum
+
+
+def assert_sum_bound(name, got, ref, abs_sum, M):
+    """Every column of an fp32 weight gradient within the summation bound of
+    the oracle's fp64 value."""
+    err = (got.detach().to("cpu", F64) - ref.to(F64)).abs()
+    bound = sum_bound(abs_sum.to(F64), M) + 1e-30
+    bad = err > bound
+    assert not bad.any(), (f"{name}: {int(bad.sum())} columns beyond the fp32 summation bound "
+                           f"(worst ratio {float((err / bound).max()):.3g})")
+
+
+def term_abs_sum(x, dy, rstd):
+    """sum_i |dy[i, j] * x[i, j] * rstd[i]| per column (fp64, CPU): the
+    absolute sum of dgamma's terms."""
+    return (dy.to(F64) * x.to(F64) * rstd.to(F64)[:, None]).abs().sum(0)
 
 
 def assert_close(name, got, ref, dtype, scale=None):
@@ -93,7 +132,8 @@ def plain_case(w, flags=R.DGAMMA_AUTO, misalign=False, with_dgamma_t=True):
     torch.cuda.synchronize()
     dx_ref, dg_ref = oracle.rmsnorm_bwd(x, g, dy, r_ref)
     return dict(M=M, N=N, T=T, y=(y, y_ref), rstd=(rstd, r_ref), dx=(dx, dx_ref),
-                dg32=(dg32, dg_ref), dgt=dgt, inputs=(xg, gg, dyg, r_ref.to(DEV)))
+                dg32=(dg32, dg_ref), dgt=dgt, inputs=(xg, gg, dyg, r_ref.to(DEV)),
+                abs_sum=term_abs_sum(x, dy, r_ref))
 
 
 def fused_case(w, flags=R.DGAMMA_AUTO, misalign=False, with_dres=True, with_dgamma_t=True):
@@ -116,7 +156,7 @@ def fused_case(w, flags=R.DGAMMA_AUTO, misalign=False, with_dres=True, with_dgam
     dx_ref, dg_ref = oracle.fused_add_rmsnorm_bwd(a_ref, g, dy, dres, r_ref)
     return dict(M=M, N=N, T=T, y=(out, o_ref), rstd=(rstd, r_ref), dx=(dx, dx_ref),
                 dg32=(dg32, dg_ref), dgt=dgt, added=(res_out, a_ref),
-                inputs=(ag, gg, dyg, dresg, r_ref.to(DEV)))
+                inputs=(ag, gg, dyg, dresg, r_ref.to(DEV)), abs_sum=term_abs_sum(a_ref, dy, r_ref))
 
 
 def check_case(c, check_fwd=True):
@@ -142,6 +182,8 @@ def check_case(c, check_fwd=True):
     dg32, dg_ref = c["dg32"]
     e = rel(dg32, dg_ref)
     assert e <= tol_dgamma(M), f"dgamma: error {e:.3g} > {tol_dgamma(M):.3g}"
+    if M > 0 and "abs_sum" in c:
+        assert_sum_bound("dgamma", dg32, dg_ref, c["abs_sum"], M)
     if c["dgt"] is not None:
         # the dtype copy is exactly the RNE rounding of the fp32 result
         assert torch.equal(c["dgt"].cpu(), dg32.cpu().to(T))
