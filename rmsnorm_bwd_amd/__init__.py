@@ -286,17 +286,38 @@ def rmsnorm_bwd_workspace_bytes(M, N, dtype, flags=DGAMMA_AUTO):
 # then allocates nothing. At most _WS_STREAMS streams keep one, the least
 # recently used giving its up first (a program that creates streams per step
 # would otherwise keep a workspace for every stream it ever used). Dropping
-# one is safe while work that uses it is still queued: torch's caching
+# one is safe while eager work that uses it is still queued: torch's caching
 # allocator hands a freed block only to later allocations on the stream that
 # allocated it, which run after that work.
+#
+# A call made while its stream is being captured into a HIP graph never uses
+# this cache: the graph bakes the workspace's address into its kernels and
+# replays them long after the call returns, when a cached buffer may have been
+# replaced and its memory handed to someone else. Such a call gets a buffer of
+# its own from the graph's private memory pool instead, which torch keeps for
+# as long as the graph exists and reuses only for later work of the same
+# capture, in stream order.
 _workspaces = OrderedDict()
 _WS_STREAMS = 16
 
 
 _workspaces_lock = threading.Lock()  # torch runs backward passes on per-device threads
+_capturing = torch.cuda.is_current_stream_capturing
+
+
+def _is_capturing(device):
+    """Whether the current stream of `device` is being captured into a graph."""
+    if device.type != "cuda":
+        return False
+    if device.index == _cur_dev():
+        return _capturing()
+    with torch.cuda.device(device):
+        return _capturing()
 
 
 def _cached_workspace(device, need, stream):
+    if _is_capturing(device):
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     key = (device.index, stream)
     with _workspaces_lock:
         ws = _workspaces.get(key)

@@ -134,3 +134,58 @@ def test_fused_and_layernorm_backward_replay():
                                                              got[4].cpu())
             assert_close("layernorm dx", got[5], dxl_ref, dt)
             assert rel(got[6], dgl_ref) <= tol_dgamma(M) and rel(got[7], dbl_ref) <= tol_dgamma(M)
+
+
+def test_captured_autograd_backward_keeps_its_own_workspace():
+    """The autograd backward captured into a graph on a stream whose cached
+    workspace an eager call created first; then a larger eager call on that
+    stream replaces the cached workspace, and a new tensor of the old size,
+    filled with a pattern, takes its memory. Replays of the graph must not
+    write into that tensor (a graph keeps the workspace it captured), and
+    must still match an eager autograd pass and the oracle."""
+    print("case graph: captured autograd backward, then a larger eager call", flush=True)
+    dt, eps, N, M, M_big = torch.bfloat16, 1e-6, 4096, 256, 2048
+    w = workloads.normal(np.random.Generator(np.random.PCG64(5)), (N,), 1.0, 0.1, dt).to(DEV)
+    w.requires_grad_()
+    x = draw(60, M, N, dt).to(DEV).requires_grad_()
+    dy = draw(61, M, N, dt, 0.0, 1e-2).to(DEV)
+    cap = torch.cuda.Stream()
+
+    def step():
+        y = R.rmsnorm(x, w, eps)
+        return torch.autograd.grad(y, (x, w), dy)
+
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()  # eager: creates the cached workspace of stream `cap`
+    torch.cuda.synchronize()
+    need = R.rmsnorm_bwd_workspace_bytes(M, N, dt)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        gx, gw = step()
+    torch.cuda.synchronize()
+    xb, dyb = draw(62, M_big, N, dt).to(DEV), draw(63, M_big, N, dt, 0.0, 1e-2).to(DEV)
+    with torch.cuda.stream(cap):
+        _, rb = R.rmsnorm_fwd_rstd(xb, w.detach(), eps)
+        R.rmsnorm_bwd(xb, w.detach(), dyb, rb)  # replaces the cached workspace
+        junk = [torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    torch.cuda.synchronize()
+    for i in range(REPLAYS):
+        xc, dyc = draw(70 + i, M, N, dt), draw(80 + i, M, N, dt, 0.0, 1e-2)
+        with torch.no_grad():
+            x.copy_(xc.to(DEV))
+        dy.copy_(dyc.to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j in junk:
+            assert bool((j == 0x5A).all()), f"replay {i}: the graph wrote into memory it does not own"
+        got = (gx.clone(), gw.clone())
+        ex, ew = step()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ex) and torch.equal(got[1], ew), f"replay {i} differs from eager"
+        if i == REPLAYS - 1:
+            r_ref, _ = oracle.rmsnorm_fwd(xc, w.detach().cpu(), eps, want_y=False)
+            dx_ref, dg_ref = oracle.rmsnorm_bwd(xc, w.detach().cpu(), dyc, r_ref)
+            assert_close("dx", got[0], dx_ref, dt)
+            assert_close("dweight", got[1], dg_ref, dt)
