@@ -354,33 +354,105 @@ def api_compare(warmup=10, iters=100, windows=5):
         print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, d, budget_s=10.0, max_calls=200):
-    """The CPU oracle (fp64, single thread) on the same workload: whole calls
-    repeated for about `budget_s` seconds of CPU work (at least three), the
-    median per call reported."""
+def floor(w, steps=100):
+    """What plain streaming kernels of the backward's read/write mix reach at
+    the workload's shape, on the same box, timed like the backward (one
+    HIP-graph replay of `steps` calls over buffer sets rotated past the
+    memory-side cache): torch's add (two reads, one write: the plain and
+    LayerNorm backward's row traffic), its addcmul (three reads, one write:
+    the fused backward with a dresidual_out), and a device-to-device copy.
+    One JSON line."""
+    dev = torch.device("cuda:0")
+    T, s = w.torch_dtype, w.elem_bytes
+    per = 4 * w.M * w.N * s
+    nsets = max(2, min(steps, -(-ROTATE_BYTES // per)))
+    sets = [[torch.randn(w.M, w.N, device=dev).to(T) for _ in range(4)] for _ in range(nsets)]
+    mn = w.M * w.N * s
+    out = {"floor": w.name, "M": w.M, "N": w.N, "dtype": w.dtype, "buffer_sets": nsets,
+           "timing": "HIP graph replay, rotated sets"}
+    for name, fn, nbytes in (
+            ("copy", lambda t: t[3].copy_(t[0]), 2 * mn),
+            ("add_2r1w", lambda t: torch.add(t[0], t[1], out=t[3]), 3 * mn),
+            ("addcmul_3r1w", lambda t: torch.addcmul(t[0], t[1], t[2], out=t[3]), 4 * mn)):
+        us = time_graph(fn, sets, steps, 5) * 1e3
+        out[name + "_us"] = round(us, 2)
+        out[name + "_GBps"] = round(nbytes / us / 1e3, 1)
+    abytes = algorithmic_bytes(w)
+    out["bwd_algorithmic_bytes"] = abytes
+    key = "addcmul_3r1w" if w.op == "fused" else "add_2r1w"
+    out["bwd_at_floor_rate_us"] = round(abytes / out[key + "_GBps"] / 1e3, 2)
+    print(json.dumps(out), flush=True)
+    del sets
+    torch.cuda.empty_cache()
+
+
+def _oracle_call(w, d):
+    """A function running the CPU oracle's backward on rows [r0, r1) of the
+    workload (the forward's statistics computed once beforehand), returning
+    its fp64 weight gradient(s) for those rows."""
     import oracle
-    x = d["x"] if w.op in ("plain", "layernorm") else None
     if w.op == "plain":
         rstd, _ = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps, want_y=False)
-        run = lambda: oracle.rmsnorm_bwd(x, d["gamma"], d["dy"], rstd)  # noqa: E731
-    elif w.op == "layernorm":
+        return lambda r0, r1: oracle.rmsnorm_bwd(d["x"][r0:r1], d["gamma"], d["dy"][r0:r1],
+                                                 rstd[r0:r1])[1:]
+    if w.op == "layernorm":
         mean, rstd, _ = oracle.layernorm_fwd(d["x"], d["gamma"], d["beta"], w.eps, want_y=False)
-        run = lambda: oracle.layernorm_bwd(d["x"], d["gamma"], d["dy"], mean, rstd)  # noqa: E731
-    else:
-        added, rstd, _ = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps,
-                                                      want_out=False)
-        run = lambda: oracle.fused_add_rmsnorm_bwd(added, d["gamma"], d["dy"],  # noqa: E731
-                                                   d["dresidual_out"], rstd)
+        return lambda r0, r1: oracle.layernorm_bwd(d["x"][r0:r1], d["gamma"], d["dy"][r0:r1],
+                                                   mean[r0:r1], rstd[r0:r1])[1:]
+    added, rstd, _ = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps,
+                                                  want_out=False)
+    return lambda r0, r1: oracle.fused_add_rmsnorm_bwd(added[r0:r1], d["gamma"], d["dy"][r0:r1],
+                                                       d["dresidual_out"][r0:r1], rstd[r0:r1])[1:]
+
+
+def _time_median(run, budget_s, max_calls):
+    """Median seconds of run() over whole calls repeated for about budget_s
+    seconds (at least three calls), and the number of calls."""
     ts = []
     while len(ts) < 3 or (sum(ts) < budget_s and len(ts) < max_calls):
         t0 = time.perf_counter()
         run()
         ts.append(time.perf_counter() - t0)
-    us = statistics.median(ts) * 1e6
-    return {"value": round(us, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {len(ts)} calls "
-                      f"({sum(ts):.1f} s of CPU work), median; fp64 C oracle, one thread",
-            "GBps": round(algorithmic_bytes(w) / us / 1e3, 2),
+    return statistics.median(ts), ts
+
+
+def host_threads(cap=16):
+    """The CPUs this process may run on, at most `cap` (a GPU machine's CPU share
+    is 16, whatever the host has)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def cpu_baseline(w, d, budget_s=8.0, max_calls=200):
+    """The CPU oracle (fp64 C, single-threaded code, unchanged) on the same
+    workload, timed two ways: one thread running whole calls, and all host
+    threads (up to 16) each running the oracle on its own contiguous shard
+    of rows, the shards' fp64 weight gradients summed afterwards (the
+    oracle call releases the interpreter lock, so the shards run in
+    parallel). Each way repeats whole calls for about `budget_s` seconds and
+    reports the median per call; `value` is the all-threads figure."""
+    from concurrent.futures import ThreadPoolExecutor
+    call = _oracle_call(w, d)
+    t1, ts1 = _time_median(lambda: call(0, w.M), budget_s, max_calls)
+    nt = host_threads()
+    bounds = [(w.M * i // nt, w.M * (i + 1) // nt) for i in range(nt)]
+    with ThreadPoolExecutor(nt) as ex:
+        def sharded():
+            parts = list(ex.map(lambda b: call(*b), bounds))
+            return [sum(p[q] for p in parts) for q in range(len(parts[0]))]
+        tn, tsn = _time_median(sharded, budget_s, max_calls)
+    abytes = algorithmic_bytes(w)
+    return {"value": round(tn * 1e6, 1), "unit": "us/call", "cores": nt, "kind": "oracle",
+            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {len(tsn)} calls "
+                      f"({sum(tsn):.1f} s) on {nt} threads, each running the fp64 C oracle on "
+                      f"1/{nt} of the rows; median per call",
+            "GBps": round(abytes / (tn * 1e6) / 1e3, 2),
+            "one_thread": {"value": round(t1 * 1e6, 1), "unit": "us/call", "cores": 1,
+                           "sample": f"{len(ts1)} whole calls ({sum(ts1):.1f} s), median",
+                           "GBps": round(abytes / (t1 * 1e6) / 1e3, 2)},
             "host": {"cpu_model": _cpu_model(), "logical_cpus": os.cpu_count()}}
 
 
@@ -430,6 +502,9 @@ def main():
     ap.add_argument("--api-compare", action="store_true",
                     help="time the backward through autograd against torch's eager RMSNorm on the "
                          "pages' public-API shapes (one JSON line per shape) and exit")
+    ap.add_argument("--floor", action="store_true",
+                    help="time torch's copy, add and addcmul at the workload's shape (streaming "
+                         "kernels of the backward's read/write mix) and exit")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the copy-bandwidth and one-row latency figures (profiled runs)")
     ap.add_argument("--graph", action="store_true",
@@ -454,6 +529,9 @@ def main():
     if args.shape_sweep:
         shape_sweep()
         return
+    if args.floor:
+        floor(workloads.WORKLOADS[args.workload])
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -465,7 +543,9 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     d = workloads.make_inputs(w)
-    per_set = 4 * w.M * w.N * w.elem_bytes
+    # row tensors a set holds on the device: x (or added), dy, dx, and
+    # dresidual_out for the fused variant
+    per_set = (4 if w.op == "fused" else 3) * w.M * w.N * w.elem_bytes
     nsets = 1 if args.hot else max(2, -(-ROTATE_BYTES // per_set))
     g, sets = make_sets(w, d, nsets)
     bwd = lambda s: call_bwd(w, g, s)  # noqa: E731
@@ -512,6 +592,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "dtype": w.dtype,
                    "eps": w.eps, "buffer_sets": nsets,
+                   "rotated_MiB": round(nsets * per_set / 2 ** 20),
                    "timing": ("hot" if args.hot else "rotated over > 512 MiB")
                    + ("; HIP graph replay" if args.graph else "; eager calls")},
         "achieved_GBps": round(gbps, 1),
