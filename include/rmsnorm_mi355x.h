@@ -13,7 +13,9 @@
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer on the calling thread's current
  *     HIP device. The caller owns every buffer, the workspace included. The
- *     library allocates nothing, frees nothing and never synchronises.
+ *     library allocates nothing, frees nothing and never synchronises (the
+ *     one exception, rmsnorm_bwd_no_alloc's scratch, is a static array of
+ *     the loaded library, not an allocation made by a call).
  *   - Row tensors are (M, N), row-major and contiguous (row stride N
  *     elements); gamma, beta and the weight-gradient outputs have N
  *     elements; rstd and mean have M. Each entry point has a *_strided twin
@@ -65,7 +67,9 @@ typedef enum {
     RMSN_ERR_FLAGS = 6,     /* unknown or contradictory flag bits */
     RMSN_ERR_DEVICE = 7,    /* a pointer is not on the current device */
     RMSN_ERR_HIP = 8,       /* the HIP runtime reported an error */
-    RMSN_ERR_ALIGN = 9      /* a pointer is not aligned to its element size */
+    RMSN_ERR_ALIGN = 9,     /* a pointer is not aligned to its element size */
+    RMSN_ERR_SCRATCH = 10   /* rmsnorm_bwd_no_alloc: the call needs more scratch
+                               than the library's static array holds */
 } rmsn_status_t;
 
 /* Flags of the backward entry points. How dgamma's per-workgroup fp32
@@ -213,6 +217,32 @@ int layernorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const v
                           float *dgamma_f32, float *dbeta_f32, void *dgamma, void *dbeta,
                           void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
                           unsigned flags, void *stream);
+
+/* Bytes of device memory the library holds on each GPU it runs on, for
+ * rmsnorm_bwd_no_alloc: a 256-byte header and the fp32 dgamma partials of up
+ * to 256 workgroups for rows of up to 8192 elements (8 MiB + 256 bytes). */
+#define RMSN_NO_ALLOC_SCRATCH_BYTES (256 + 256 * 8192 * 4)
+
+/* rmsnorm_bwd with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It calls no allocating routine; its
+ * scratch is a static device array of RMSN_NO_ALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its address
+ * is looked up once per device, on the first call with that device
+ * current). Every call on one GPU shares that array and it keeps the last
+ * call's contents: calls ordered on one stream are safe, but calls that
+ * overlap on one GPU (other streams, other threads) race and give wrong
+ * results. Nothing in it has to start at zero: a call writes every partial
+ * it reads. A call whose workspace need (rmsnorm_bwd_workspace_bytes of the
+ * same M, N, dtype and flags) exceeds RMSN_NO_ALLOC_SCRATCH_BYTES returns
+ * RMSN_ERR_SCRATCH before anything is enqueued; only rows of more than 8192
+ * elements in the default and deterministic modes can need that much (the
+ * atomic mode and one-workgroup calls need only the header). Other arguments, results and errors are those of
+ * rmsnorm_bwd, and for the same arguments the results are bit for bit
+ * those of rmsnorm_bwd. */
+int rmsnorm_bwd_no_alloc(const void *x, const void *gamma, const void *dy, const float *rstd,
+                         void *dx, float *dgamma_f32, void *dgamma, int64_t M, int64_t N, int dtype,
+                         unsigned flags, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *rmsn_status_string(int status);

@@ -60,6 +60,7 @@ def lib():
         L.rmsnorm_bwd_workspace_bytes.restype = SZ
         L.rmsnorm_bwd.argtypes = [P, P, P, P, P, P, P, P, SZ, I64, I64, I, U, P]
         L.fused_add_rmsnorm_bwd.argtypes = [P, P, P, P, P, P, P, P, P, SZ, I64, I64, I, U, P]
+        L.rmsnorm_bwd_no_alloc.argtypes = [P, P, P, P, P, P, P, I64, I64, I, U, P]
         L.layernorm_fwd_stats.argtypes = [P, P, P, P, P, P, I64, I64, F, I, P]
         L.layernorm_bwd_workspace_bytes.argtypes = [I64, I64, I, U]
         L.layernorm_bwd_workspace_bytes.restype = SZ
@@ -76,7 +77,7 @@ def lib():
         L.rmsn_status_string.argtypes = [I]
         L.rmsn_status_string.restype = ctypes.c_char_p
         for fn in ("rmsnorm_fwd_rstd", "fused_add_rmsnorm_fwd_rstd", "rmsnorm_bwd",
-                   "fused_add_rmsnorm_bwd", "layernorm_fwd_stats", "layernorm_bwd",
+                   "fused_add_rmsnorm_bwd", "rmsnorm_bwd_no_alloc", "layernorm_fwd_stats", "layernorm_bwd",
                    "rmsnorm_fwd_rstd_strided", "fused_add_rmsnorm_fwd_rstd_strided",
                    "rmsnorm_bwd_strided", "fused_add_rmsnorm_bwd_strided",
                    "layernorm_fwd_stats_strided", "layernorm_bwd_strided"):
@@ -461,6 +462,28 @@ def rmsnorm_bwd(x, gamma, dy, rstd, dx=None, dgamma_f32=None, dgamma=None, works
                 flags=DGAMMA_AUTO):
     """Backward ([I769] Implementation plan, Math). Returns (dx, dgamma_f32, dgamma)."""
     return _bwd("rmsnorm_bwd", x, gamma, dy, None, rstd, dx, dgamma_f32, dgamma, workspace, flags)
+
+
+def rmsnorm_bwd_no_alloc(x, gamma, dy, rstd, dx, dgamma_f32, dgamma=None, flags=DGAMMA_AUTO):
+    """rmsnorm_bwd over caller-given outputs with the library's static scratch
+    as its workspace (no device allocation by the library or by this
+    binding). Calls that overlap on one GPU share that scratch and race.
+    Contiguous rows only. Returns (dx, dgamma_f32, dgamma)."""
+    fn = "rmsnorm_bwd_no_alloc"
+    dt = _code(x, fn)
+    M, N, ldx = _rows(x, gamma, fn)
+    _same(fn, x, gamma, dy, dx, dgamma)
+    if ldx != N or _ld(dy, x.shape, N, fn, "dy") != N or _ld(dx, x.shape, N, fn, "dx") != N:
+        raise ValueError(f"{fn}: row tensors must be contiguous")
+    _check_rstd(rstd, M, x.device)
+    _f32_vec(dgamma_f32, N, x.device, fn, "dgamma_f32")
+    if dgamma is not None:
+        _vec(dgamma, N, fn, "dgamma")
+    call = lambda: lib().rmsnorm_bwd_no_alloc(  # noqa: E731
+        _p(x), _p(gamma), _p(dy), _p(rstd), _p(dx), _p(dgamma_f32), _p(dgamma), M, N, dt, int(flags),
+        _stream(x.device))
+    _raise_on(fn, _on_device(x.device, call))
+    return dx, dgamma_f32, dgamma
 
 
 def fused_add_rmsnorm_bwd(added, gamma, dy, dresidual_out, rstd, dx=None, dgamma_f32=None,

@@ -119,7 +119,7 @@ size_t workspace_query(int64_t M, int64_t N, int dtype, unsigned flags, int narr
 int bwd_common(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy, const void *dres,
                int64_t lddres, const float *mean, const float *rstd, void *dx, int64_t lddx, float *dgamma_f32,
                void *dgamma, float *dbeta_f32, void *dbeta, void *workspace, size_t workspace_bytes, int64_t M,
-               int64_t N, int dtype, unsigned flags, void *stream, bool layer) {
+               int64_t N, int dtype, unsigned flags, void *stream, bool layer, bool own_scratch = false) {
     if (!dtype_ok(dtype)) return RMSN_ERR_DTYPE;
     if (int st = check_shape(M, N)) return st;
     if (int st = check_flags(flags)) return st;
@@ -144,8 +144,9 @@ int bwd_common(const void *x, int64_t ldx, const void *gamma, const void *dy, in
     // buffer sized by the query is always accepted and nothing less is
     if (workspace_bytes < workspace_query(M, N, dtype, flags, layer ? 2 : 1)) return RMSN_ERR_WORKSPACE;
     if (flags & RMSN_CHECK_DEVICE) {
+        // the library's own scratch is on the current device by construction
         if (int st = check_device({x, gamma, dy, dres, mean, rstd, dx, dgamma_f32, dgamma, dbeta_f32, dbeta,
-                                   workspace}))
+                                   own_scratch ? nullptr : workspace}))
             return st;
     }
     rmsn::BwdArgs a;
@@ -272,6 +273,19 @@ int rmsnorm_bwd(const void *x, const void *gamma, const void *dy, const float *r
                       workspace, workspace_bytes, M, N, dtype, flags, stream, false);
 }
 
+int rmsnorm_bwd_no_alloc(const void *x, const void *gamma, const void *dy, const float *rstd, void *dx,
+                         float *dgamma_f32, void *dgamma, int64_t M, int64_t N, int dtype, unsigned flags,
+                         void *stream) {
+    // 0 for arguments rmsnorm_bwd rejects: it then reports which, before any
+    // HIP call (its dtype, shape and flags checks come first)
+    const size_t need = workspace_query(M, N, dtype, flags, 1);
+    if (need > (size_t)RMSN_NO_ALLOC_SCRATCH_BYTES) return RMSN_ERR_SCRATCH;
+    void *scratch = nullptr;
+    if (need != 0 && rmsn::device_scratch(&scratch) != hipSuccess) return RMSN_ERR_HIP;
+    return bwd_common(x, N, gamma, dy, N, nullptr, N, nullptr, rstd, dx, N, dgamma_f32, dgamma, nullptr, nullptr,
+                      scratch, RMSN_NO_ALLOC_SCRATCH_BYTES, M, N, dtype, flags, stream, false, true);
+}
+
 int rmsnorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const void *dy, int64_t lddy,
                         const float *rstd, void *dx, int64_t lddx, float *dgamma_f32, void *dgamma,
                         void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype, unsigned flags,
@@ -341,6 +355,7 @@ const char *rmsn_status_string(int status) {
     case RMSN_ERR_DEVICE: return "pointer is not on the current device";
     case RMSN_ERR_HIP: return "HIP runtime error";
     case RMSN_ERR_ALIGN: return "pointer not aligned to its element size";
+    case RMSN_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
     default: return "unknown status";
     }
 }

@@ -24,9 +24,13 @@
 // The pages' design (one workgroup per row, a global fp32 atomic per element
 // for dweight, a second read of the row for the output pass) is prior art for
 // another code generator; it is not followed here.
+#include <atomic>
+#include <mutex>
+
 #include "device.h"
 #include "launch.h"
 #include "plan.h"
+#include "rmsnorm_mi355x.h"
 
 namespace rmsn {
 
@@ -999,6 +1003,41 @@ hipError_t launch_bwd(int dtype, const RowPlan &p, const BwdArgs &a, int grid, v
     case DT_BF16: return launch_bwd_dt<DT_BF16>(p, a, grid, workspace, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of rmsnorm_bwd_no_alloc: one static array per GPU, the workspace of
+// callers that cannot allocate. In host code `scratch` names a host-side
+// stand-in, not device memory; the kernels get its device address, looked up
+// once per device with that device current and remembered here.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[RMSN_NO_ALLOC_SCRATCH_BYTES];
+static_assert(RMSN_NO_ALLOC_SCRATCH_BYTES >= WS_HEADER, "the scratch holds at least the header");
+
+constexpr int SCRATCH_DEVICES = 64;
+static std::atomic<void *> scratch_addr[SCRATCH_DEVICES];
+static std::mutex scratch_mu;
+
+hipError_t device_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();
+                return e != hipSuccess ? e : hipErrorInvalidSymbol;
+            }
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_fwd(int dtype, const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {

@@ -48,6 +48,10 @@ struct FwdArgs {
 hipError_t launch_bwd(int dtype, const RowPlan &p, const BwdArgs &a, int grid, void *workspace,
                       hipStream_t s);
 
+// Device address, on the current device, of the static scratch array of
+// rmsnorm_bwd_no_alloc (looked up once per device, then remembered).
+hipError_t device_scratch(void **ptr);
+
 // Enqueue the forward on stream s with `grid` blocks.
 hipError_t launch_fwd(int dtype, const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s);
 

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULL, SHAPE, DTYPE, EPS, WORKSPACE, FLAGS, DEVICE, HIP, ALIGN = range(10)
+OK, NULL, SHAPE, DTYPE, EPS, WORKSPACE, FLAGS, DEVICE, HIP, ALIGN, SCRATCH = range(11)
 A = 0x10000          # a 256-byte-aligned fake device address
 P = ctypes.c_void_p
 
@@ -35,6 +35,7 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"^\s*#[^\n]*", "", text, flags=re.M)  # preprocessor lines
         for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\(([^;{}]*)\)\s*;", text):
             names.append(m.group(1))
     return sorted(set(names))
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert R.status_string(s) and R.status_string(s) != "unknown status"
     assert R.status_string(99) == "unknown status"
 
@@ -320,3 +321,29 @@ def test_forward_row_strides():
     fl = R.lib().layernorm_fwd_stats_strided
     assert fl(P(A), 10, P(A), None, P(A + 1), 64, P(A), P(A), 2, 64, 1e-5, R.BF16, None) == SHAPE
     assert fl(P(A), 64, P(A), None, P(A + 1), 64, P(A), P(A), 2, 64, 1e-5, R.BF16, None) == ALIGN
+
+
+def no_alloc(**kw):
+    a = dict(x=A, gamma=A, dy=A, rstd=A, dx=A, dg32=A, dg=None, M=256, N=16384, dtype=R.BF16, flags=0)
+    a.update(kw)
+    return R.lib().rmsnorm_bwd_no_alloc(P(a["x"]), P(a["gamma"]), P(a["dy"]), P(a["rstd"]), P(a["dx"]),
+                                        P(a["dg32"]), P(a["dg"]), a["M"], a["N"], a["dtype"], a["flags"],
+                                        None)
+
+
+def test_no_alloc_refuses_before_any_hip_call():
+    """The entry point without a workspace: a call needing more than its
+    static scratch is refused with its own status, and arguments the
+    backward rejects keep their statuses, all before any HIP call (every
+    case is refused, so nothing can reach a launch on the fake addresses)."""
+    limit = 256 + 256 * 8192 * 4
+    assert R.rmsnorm_bwd_workspace_bytes(256, 16384, R.BF16) > limit
+    assert R.rmsnorm_bwd_workspace_bytes(32768, 8192, R.BF16) <= limit
+    assert no_alloc() == SCRATCH
+    assert no_alloc(flags=R.DGAMMA_DETERMINISTIC) == SCRATCH
+    assert no_alloc(dtype=3) == DTYPE
+    assert no_alloc(N=0) == SHAPE
+    assert no_alloc(N=R.MAX_N + 1) == SHAPE
+    assert no_alloc(M=-1) == SHAPE
+    assert no_alloc(flags=8) == FLAGS
+    assert no_alloc(flags=3) == FLAGS
