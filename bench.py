@@ -204,36 +204,44 @@ def latency_floor(w_name="plain_1x4096_bf16"):
             "timing": "HIP graph replay", "graph_matches_eager": bool(torch.equal(eager, s["dx"]))}
 
 
-def mode_sweep():
-    """The dgamma combining modes against each other on an (M, N) grid, GPU
-    time per call from HIP-graph replay (one JSON line per shape): the
-    measurement behind the default mode's choices."""
+def mode_sweep(reps=3):
+    """The dgamma modes against each other on an (M, N) grid: GPU time per
+    call from HIP-graph replay, each mode timed `reps` times in rotating
+    order and the median kept (one JSON line per shape). The one-block mode
+    (one CU does all the work) is timed up to 512 rows. This is the
+    measurement behind the default mode's rule."""
     dev = torch.device("cuda:0")
+    modes = (("auto", R.DGAMMA_AUTO), ("deterministic", R.DGAMMA_DETERMINISTIC),
+             ("atomic", R.DGAMMA_ATOMIC), ("one_block", R.DGAMMA_ONE_BLOCK))
     for dt in (torch.bfloat16, torch.float32):
         es = 2 if dt == torch.bfloat16 else 4
         for N in (256, 1024, 4096, 8192, 16384):
-            for M in (1, 2, 8, 32, 128, 512, 2048, 8192):
-                per = 4 * M * N * es
+            for M in (1, 2, 4, 8, 16, 32, 64, 128, 512, 2048, 8192):
+                per = 3 * M * N * es
                 nsets = max(1, min(8, -(-ROTATE_BYTES // per)))
                 g = torch.ones(N, dtype=dt, device=dev)
                 sets = []
                 for _ in range(nsets):
                     x = torch.randn(M, N, device=dev).to(dt)
                     _, rstd = R.rmsnorm_fwd_rstd(x, g, 1e-6)
+                    ws = max(R.rmsnorm_bwd_workspace_bytes(M, N, dt, fl) for _, fl in modes)
                     sets.append((x, torch.randn(M, N, device=dev).to(dt), rstd, torch.empty_like(x),
                                  torch.empty(N, device=dev), torch.empty(N, dtype=dt, device=dev),
-                                 torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(M, N, dt)),
-                                             dtype=torch.uint8, device=dev)))
+                                 torch.empty(max(256, ws), dtype=torch.uint8, device=dev)))
                 row = {"dtype": str(dt).split(".")[-1], "M": M, "N": N}
-                for name, fl in (("auto", R.DGAMMA_AUTO), ("deterministic", R.DGAMMA_DETERMINISTIC),
-                                 ("atomic", R.DGAMMA_ATOMIC)):
-                    it = iter(range(1 << 30))
+                todo = [(n, fl) for n, fl in modes if n != "one_block" or M <= 512]
+                times = {n: [] for n, _ in todo}
+                for rep in range(reps):
+                    for name, fl in todo[rep % len(todo):] + todo[:rep % len(todo)]:
+                        it = iter(range(1 << 30))
 
-                    def call():
-                        t = sets[next(it) % nsets]
-                        R.rmsnorm_bwd(t[0], g, t[1], t[2], dx=t[3], dgamma_f32=t[4], dgamma=t[5],
-                                      workspace=t[6], flags=fl)
-                    row[name + "_us"] = round(_graph_us(call, calls=max(nsets, 8), replays=10), 2)
+                        def call():
+                            t = sets[next(it) % nsets]
+                            R.rmsnorm_bwd(t[0], g, t[1], t[2], dx=t[3], dgamma_f32=t[4], dgamma=t[5],
+                                          workspace=t[6], flags=fl)
+                        times[name].append(_graph_us(call, calls=max(nsets, 8), replays=5))
+                for name, _ in todo:
+                    row[name + "_us"] = round(statistics.median(times[name]), 2)
                 print(json.dumps(row), flush=True)
                 del sets
                 torch.cuda.empty_cache()
@@ -300,16 +308,51 @@ API_SHAPES = [
 ]
 
 
-def api_compare(warmup=10, iters=100, windows=5):
+def _autograd_graph_us(forward, impl, d, op, dev, with_backward, calls=10, replays=20):
+    """GPU time per pass of `forward` (and, with_backward, of the backward
+    through torch.autograd.grad) from one HIP graph of `calls` passes,
+    replayed. The leaves are fresh tensors that no eager pass has touched,
+    and the warm-up and the capture run on one side stream, so every autograd
+    node of the captured passes belongs to the capturing stream."""
+    x = d["x"].to(dev).requires_grad_()
+    weight = d["gamma"].to(dev).requires_grad_()
+    res = d["residual"].to(dev).requires_grad_() if op == "fused" else None
+    douts = (d["dy"].to(dev),) if op == "plain" else (d["dy"].to(dev), d["dresidual_out"].to(dev))
+    inputs = (x, weight) if op == "plain" else (x, res, weight)
+
+    def one():
+        o = forward(impl, x, weight, res)
+        if with_backward:
+            torch.autograd.grad(o, inputs, douts)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            one()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(calls):
+            one()
+    torch.cuda.synchronize()
+    ms = time_calls(lambda _: graph.replay(), [None], replays, 3)
+    del graph
+    return ms * 1e3 / calls
+
+
+def api_compare(warmup=10, iters=100, windows=7):
     """Backward through the public autograd API, this library's wrappers
     against torch's eager RMSNorm (torch.nn.functional.rms_norm; for the
     fused-add form, torch's add then rms_norm), timed the way [P854]'s
     benchmark contract times them: the forward graph is built before timing;
     each backward allocates its gradients and includes the weight gradient's
     reduction and its cast to the parameter dtype; hot cache; HIP events
-    around `iters` backward calls after `warmup`. Both sides are bound by the
-    host (the autograd engine and Python) at most of these shapes, so each
-    figure is the median over `windows` such loops. Gradients of the two are
+    around `iters` backward calls after `warmup`. The two implementations
+    are timed in alternating windows in one process, so both see the same
+    host state, and each figure is the median over `windows` windows. Each
+    backward's GPU time is also given: one HIP graph of forward and backward
+    replayed, less one of the forward alone. Gradients of the two are
     compared before timing. One JSON line per shape."""
     import torch.nn.functional as F
     from rmsnorm_bwd_amd.autograd import fused_add_rmsnorm, rmsnorm
@@ -318,30 +361,41 @@ def api_compare(warmup=10, iters=100, windows=5):
         w = workloads.custom(op, M, N, dt, 1e-6, dy_sigma=1e-2)
         d = workloads.make_inputs(w)
 
+        def forward(impl, x, weight, res):
+            if op == "plain":
+                return (rmsnorm(x, weight, w.eps) if impl == "ours" else F.rms_norm(x, (N,), weight, w.eps),)
+            if impl == "ours":
+                return fused_add_rmsnorm(x, res, weight, w.eps)
+            res_out = x + res
+            return F.rms_norm(res_out, (N,), weight, w.eps), res_out
+
         def graph(impl):
             weight = d["gamma"].to(dev).requires_grad_()
             x = d["x"].to(dev).requires_grad_()
-            dy = d["dy"].to(dev)
-            if op == "plain":
-                y = rmsnorm(x, weight, w.eps) if impl == "ours" else F.rms_norm(x, (N,), weight, w.eps)
-                return (y,), (dy,), (x, weight)
-            res = d["residual"].to(dev).requires_grad_()
-            if impl == "ours":
-                out, res_out = fused_add_rmsnorm(x, res, weight, w.eps)
-            else:
-                res_out = x + res
-                out = F.rms_norm(res_out, (N,), weight, w.eps)
-            return (out, res_out), (dy, d["dresidual_out"].to(dev)), (x, res, weight)
+            res = d["residual"].to(dev).requires_grad_() if op == "fused" else None
+            douts = (d["dy"].to(dev),) if op == "plain" else (d["dy"].to(dev), d["dresidual_out"].to(dev))
+            inputs = (x, weight) if op == "plain" else (x, res, weight)
+            return forward(impl, x, weight, res), douts, inputs, (x, weight, res)
 
         line = {"api_compare": f"{'rmsnorm_bwd' if op == 'plain' else 'fused_add_bwd'} {M}x{N} {dt}"}
-        grads = {}
+        fns, grads = {}, {}
         for impl in ("ours", "torch"):
-            outs, douts, inputs = graph(impl)
-            fn = lambda: torch.autograd.grad(outs, inputs, douts, retain_graph=True)  # noqa: E731
-            grads[impl] = fn()
-            runs = [time_calls(lambda _: fn(), [None], iters, warmup if k == 0 else 0)
-                    for k in range(windows)]
-            line[f"{impl}_us"] = round(statistics.median(runs) * 1e3, 2)
+            outs, douts, inputs, raw = graph(impl)
+            fns[impl] = (lambda o=outs, i=inputs, g=douts: torch.autograd.grad(o, i, g, retain_graph=True))
+            grads[impl] = fns[impl]()
+            fns[impl]()
+        torch.cuda.synchronize()
+        runs = {"ours": [], "torch": []}
+        for k in range(windows):
+            for impl in (("ours", "torch") if k % 2 == 0 else ("torch", "ours")):
+                runs[impl].append(time_calls(lambda _: fns[impl](), [None], iters, warmup if k < 2 else 0))
+        for impl in ("ours", "torch"):
+            line[f"{impl}_us"] = round(statistics.median(runs[impl]) * 1e3, 2)
+        # free the timing passes' autograd graphs before capturing new ones
+        del fns, outs, douts, inputs, raw
+        for impl in ("ours", "torch"):
+            line[f"{impl}_gpu_us"] = round(_autograd_graph_us(forward, impl, d, op, dev, True)
+                                           - _autograd_graph_us(forward, impl, d, op, dev, False), 2)
         g_o, g_t = grads["ours"], grads["torch"]
 
         def rdiff(a, b):
@@ -354,13 +408,29 @@ def api_compare(warmup=10, iters=100, windows=5):
         print(json.dumps(line), flush=True)
 
 
+def _stream_floor_lib():
+    """The streaming-floor kernel's library (built beside the library)."""
+    import ctypes
+    from rmsnorm_bwd_amd import build as B
+    if not os.path.exists(B.FLOOR_LIB):
+        raise RuntimeError(f"{B.FLOOR_LIB} is missing: build with __graft_entry__.build()")
+    L = ctypes.CDLL(B.FLOOR_LIB)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.rmsn_stream_floor.argtypes = [P, P, P, P, I64, I64, I, P]
+    L.rmsn_stream_floor.restype = I
+    return L
+
+
 def floor(w, steps=100):
-    """What plain streaming kernels of the backward's read/write mix reach at
-    the workload's shape, on the same box, timed like the backward (one
-    HIP-graph replay of `steps` calls over buffer sets rotated past the
-    memory-side cache): torch's add (two reads, one write: the plain and
-    LayerNorm backward's row traffic), its addcmul (three reads, one write:
-    the fused backward with a dresidual_out), and a device-to-device copy.
+    """What streaming kernels of the backward's read/write mix reach at the
+    workload's shape, on the same box, timed like the backward (one HIP-graph
+    replay of `steps` calls over buffer sets rotated past the memory-side
+    cache): torch's add (two reads, one write: the plain and LayerNorm
+    backward's row traffic) and addcmul (three reads, one write: the fused
+    backward with a dresidual_out), a device-to-device copy, and the
+    backward's own window ring with its arithmetic replaced by out = a + b
+    (+ c) (rmsn_stream_floor: same row plan, grid, ring depth, prologue and
+    cache bits; no row reduction, no weight-gradient partials, no finalize).
     One JSON line."""
     dev = torch.device("cuda:0")
     T, s = w.torch_dtype, w.elem_bytes
@@ -370,20 +440,60 @@ def floor(w, steps=100):
     mn = w.M * w.N * s
     out = {"floor": w.name, "M": w.M, "N": w.N, "dtype": w.dtype, "buffer_sets": nsets,
            "timing": "HIP graph replay, rotated sets"}
+    ring = _stream_floor_lib()
+    code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+
+    def ring_call(t, nr):
+        st = ring.rmsn_stream_floor(t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr() if nr == 3 else None,
+                                    t[3].data_ptr(), w.M, w.N, code, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"rmsn_stream_floor: status {st}")
     for name, fn, nbytes in (
             ("copy", lambda t: t[3].copy_(t[0]), 2 * mn),
             ("add_2r1w", lambda t: torch.add(t[0], t[1], out=t[3]), 3 * mn),
-            ("addcmul_3r1w", lambda t: torch.addcmul(t[0], t[1], t[2], out=t[3]), 4 * mn)):
+            ("addcmul_3r1w", lambda t: torch.addcmul(t[0], t[1], t[2], out=t[3]), 4 * mn),
+            ("ring_2r1w", lambda t: ring_call(t, 2), 3 * mn),
+            ("ring_3r1w", lambda t: ring_call(t, 3), 4 * mn)):
         us = time_graph(fn, sets, steps, 5) * 1e3
         out[name + "_us"] = round(us, 2)
         out[name + "_GBps"] = round(nbytes / us / 1e3, 1)
+        if name.startswith("ring"):
+            # the ring moved every byte: its output is the fp32 sum, rounded once
+            t = sets[0]
+            fn(t)
+            want = t[0].float() + t[1].float()
+            if name == "ring_3r1w":
+                want = want + t[2].float()
+            torch.cuda.synchronize()
+            out[name + "_exact"] = bool(torch.equal(t[3], want.to(T)))
     abytes = algorithmic_bytes(w)
     out["bwd_algorithmic_bytes"] = abytes
-    key = "addcmul_3r1w" if w.op == "fused" else "add_2r1w"
-    out["bwd_at_floor_rate_us"] = round(abytes / out[key + "_GBps"] / 1e3, 2)
+    key = "ring_3r1w" if w.op == "fused" else "ring_2r1w"
+    out["bwd_at_ring_floor_rate_us"] = round(abytes / out[key + "_GBps"] / 1e3, 2)
     print(json.dumps(out), flush=True)
     del sets
     torch.cuda.empty_cache()
+
+
+def ring_floor(w, sets, timer, steps, warmup):
+    """The backward's row traffic alone through its own window ring
+    (rmsn_stream_floor over the same buffer sets: x or added, dy and, for
+    the fused variant, dresidual_out read, dx written; no reduction, no
+    partials, no finalize), timed like the backward: what the ring itself
+    delivers at this shape."""
+    lib = _stream_floor_lib()
+    code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+
+    def call(s):
+        st = lib.rmsn_stream_floor(s["x"].data_ptr(), s["dy"].data_ptr(),
+                                   s["dres"].data_ptr() if s["dres"] is not None else None,
+                                   s["dx"].data_ptr(), w.M, w.N, code, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"rmsn_stream_floor: status {st}")
+    us = timer(call, sets, steps, warmup) * 1e3
+    nbytes = (4 if w.op == "fused" else 3) * w.M * w.N * w.elem_bytes
+    return {"us": round(us, 2), "row_GBps": round(nbytes / us / 1e3, 1),
+            "what": "the row bytes through the same window ring, without the arithmetic"}
 
 
 def _oracle_call(w, d):
@@ -573,6 +683,7 @@ def main():
     skip = args.copy_calibration or args.no_extras
     copy_gbps = None if skip else copy_bandwidth()
     latency = None if skip else latency_floor()
+    ring = None if skip else ring_floor(w, sets, timer, args.steps, args.warmup)
     line = {
         "metric": "rmsnorm_bwd us/call + achieved HBM GB/s (% of peak), 4096x4096 bf16"
                   if w.name == workloads.HEADLINE
@@ -602,6 +713,8 @@ def main():
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "pct_of_copy": round(100 * gbps / copy_gbps, 1) if copy_gbps else None,
         "latency": latency,
+        "ring_floor": ring,
+        "pct_of_ring_floor": round(100 * ring["us"] / (ms * 1e3), 1) if ring else None,
         "fwd_rstd_us": round(ms_fwd * 1e3, 2),
         "fwd_rstd_GBps": round(fwd_bytes(w) / (ms_fwd * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,

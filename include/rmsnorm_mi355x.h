@@ -64,7 +64,7 @@ typedef enum {
     RMSN_ERR_DTYPE = 3,     /* unknown dtype code */
     RMSN_ERR_EPS = 4,       /* eps is negative, NaN or infinite */
     RMSN_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query */
-    RMSN_ERR_FLAGS = 6,     /* unknown or contradictory flag bits */
+    RMSN_ERR_FLAGS = 6,     /* unknown flag bits */
     RMSN_ERR_DEVICE = 7,    /* a pointer is not on the current device */
     RMSN_ERR_HIP = 8,       /* the HIP runtime reported an error */
     RMSN_ERR_ALIGN = 9,     /* a pointer is not aligned to its element size */
@@ -72,9 +72,13 @@ typedef enum {
                                than the library's static array holds */
 } rmsn_status_t;
 
-/* Flags of the backward entry points. How dgamma's per-workgroup fp32
- * partials are combined across workgroups:
- *   RMSN_DGAMMA_AUTO           the library's measured default;
+/* Flags of the backward entry points. The low two bits choose how dgamma's
+ * per-workgroup fp32 partials are combined across workgroups:
+ *   RMSN_DGAMMA_AUTO           the library's measured default: one workgroup
+ *                              writing the gradients itself for small
+ *                              problems (N <= 1024 and M * N <= 8192, or
+ *                              M <= 2 and N <= 8192), the deterministic
+ *                              two-stage sum otherwise;
  *   RMSN_DGAMMA_DETERMINISTIC  partials go to the workspace and a second
  *                              kernel sums them in a fixed order: the same
  *                              inputs give the same bits on every call;
@@ -85,14 +89,20 @@ typedef enum {
  *                              dgamma_f32 (and dbeta_f32) must be ordinary
  *                              device allocations (hipMalloc), not host,
  *                              managed or fine-grained memory, where such
- *                              adds do not take effect.
- * RMSN_CHECK_DEVICE additionally checks, with the HIP runtime, that every
- * pointer belongs to the current device (the fault the pages' device guard
- * fixed: [P800] review-fix commit). */
+ *                              adds do not take effect;
+ *   RMSN_DGAMMA_ONE_BLOCK      the whole backward in one workgroup, which
+ *                              writes the gradients itself: one launch,
+ *                              deterministic, meant for problems of a few
+ *                              short rows (one CU does all the work).
+ * An explicit mode is honoured at every size. RMSN_CHECK_DEVICE
+ * additionally checks, with the HIP runtime, that every pointer belongs to
+ * the current device (the fault the pages' device guard fixed: [P800]
+ * review-fix commit). */
 enum {
     RMSN_DGAMMA_AUTO = 0,
     RMSN_DGAMMA_DETERMINISTIC = 1,
     RMSN_DGAMMA_ATOMIC = 2,
+    RMSN_DGAMMA_ONE_BLOCK = 3,
     RMSN_CHECK_DEVICE = 4
 };
 

@@ -28,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librmsnorm_mi355x.so")
 
 F32, F16, BF16 = 0, 1, 2
-DGAMMA_AUTO, DGAMMA_DETERMINISTIC, DGAMMA_ATOMIC, CHECK_DEVICE = 0, 1, 2, 4
+DGAMMA_AUTO, DGAMMA_DETERMINISTIC, DGAMMA_ATOMIC, DGAMMA_ONE_BLOCK, CHECK_DEVICE = 0, 1, 2, 3, 4
 MAX_N = 16384
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
@@ -426,36 +426,6 @@ def _bwd(fn, x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace, flags,
                          (x, gamma, dy, dres, rstd, dx, dgamma_f32, dgamma, workspace))
     _raise_on(fn, _on_device(dev, f, *args, st_))
     return dx, dgamma_f32, dgamma
-
-
-def _bwd_saved(fn, x, gamma, dy, dres, rstd, dgamma):
-    """The backward call of the autograd wrappers. x, gamma and rstd are the
-    tensors their forward checked and saved; dy (and dres) come from torch's
-    autograd engine, which gives a backward the shape, dtype and device of
-    the forward's output. For contiguous rows this skips the checks that
-    already hold (the dtype and shape of dy are still compared); anything else
-    takes the full binding. Returns (dx, dgamma_f32, dgamma)."""
-    rows = (x, dy) if dres is None else (x, dy, dres)
-    if not all(t.is_contiguous() and t.dtype == x.dtype and t.shape == x.shape for t in rows):
-        return _bwd(fn, x, gamma, dy, dres, rstd, None, None, dgamma, None, DGAMMA_AUTO)
-    N, M = gamma.shape[0], rstd.shape[0]
-    dev = x.device
-    dt = _DTYPE_CODE[x.dtype]
-    dx = torch.empty_like(x)
-    dg32 = torch.empty(N, dtype=torch.float32, device=dev)
-    st_ = _raw_stream(dev)
-    ws = _cached_workspace(dev, rmsnorm_bwd_workspace_bytes(M, N, dt, DGAMMA_AUTO), st_)
-    wsb = ws.numel()
-    if fn == "rmsnorm_bwd":
-        call = lambda: lib().rmsnorm_bwd(  # noqa: E731
-            x.data_ptr(), gamma.data_ptr(), dy.data_ptr(), rstd.data_ptr(), dx.data_ptr(), dg32.data_ptr(),
-            _p(dgamma), ws.data_ptr(), wsb, M, N, dt, DGAMMA_AUTO, st_)
-    else:
-        call = lambda: lib().fused_add_rmsnorm_bwd(  # noqa: E731
-            x.data_ptr(), gamma.data_ptr(), dy.data_ptr(), _p(dres), rstd.data_ptr(), dx.data_ptr(),
-            dg32.data_ptr(), _p(dgamma), ws.data_ptr(), wsb, M, N, dt, DGAMMA_AUTO, st_)
-    _raise_on(fn, _on_device(dev, call))
-    return dx, dg32, dgamma
 
 
 def rmsnorm_bwd(x, gamma, dy, rstd, dx=None, dgamma_f32=None, dgamma=None, workspace=None,

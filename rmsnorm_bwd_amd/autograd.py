@@ -1,9 +1,11 @@
-"""Autograd wrappers over the C ABI binding.
+"""Autograd wrappers over the C ABI.
 
 ``rmsnorm(x, weight, eps)``, ``fused_add_rmsnorm(x, residual, weight, eps,
 prenorm=True)`` and ``layer_norm(x, weight, bias, eps)`` are differentiable:
 their forward runs the library's forward that saves the row statistics, their
-backward runs the library's backward. Like the rest of the package they only
+backward runs the library's backward. The autograd nodes are torch C++
+autograd Functions (``csrc/autograd_ext.cpp``), so torch's engine runs the
+backward without entering Python. Like the rest of the package they only
 marshal arguments; every step runs in the HIP kernels.
 
 Pages cited, by title:
@@ -24,74 +26,57 @@ Pages cited, by title:
 """
 import torch
 
-from . import (_bwd_saved, _view, fused_add_rmsnorm_fwd_rstd, layernorm_bwd, layernorm_fwd_stats,
-               rmsnorm_fwd_rstd)
+_ext_module = None
 
 
-def _rows(t):
-    """t itself when the library can read it in place (rows of unit stride
-    under one row stride), else a contiguous copy."""
-    if t.is_contiguous():
-        return t
-    try:
-        _view(t, t.shape[-1], "", "")
-        return t
-    except ValueError:
-        return t.contiguous()
+def _ext():
+    """The compiled autograd nodes (``_autograd_ext``); raises if not built."""
+    global _ext_module
+    if _ext_module is None:
+        try:
+            from . import _autograd_ext
+        except ImportError as e:
+            raise RuntimeError(
+                "rmsnorm_bwd_amd._autograd_ext is missing or does not load: build it with "
+                "__graft_entry__.build(). There is no fallback path.") from e
+        _ext_module = _autograd_ext
+    return _ext_module
 
 
-def _weight_grad(dgamma_f32, dgamma, weight):
-    """dgamma in the weight's dtype: the fp32 sum itself for fp32 weights,
-    else the library's round-to-nearest-even copy."""
-    return dgamma_f32 if weight.dtype == torch.float32 else dgamma
-
-
-class RMSNormFunction(torch.autograd.Function):
-    """y = x * rstd * weight over the last dimension, rstd = 1/sqrt(mean(x^2) + eps)."""
+class RMSNormFunction:
+    """rmsnorm's autograd node, a torch C++ autograd Function: its forward
+    saves x, the weight and the fp32 rstd; its backward calls rmsnorm_bwd.
+    y = x * rstd * weight over the last dimension, rstd = 1/sqrt(mean(x^2) + eps)."""
 
     @staticmethod
-    def forward(ctx, x, weight, eps):
-        x = _rows(x)
-        weight = weight.contiguous()
-        y, rstd = rmsnorm_fwd_rstd(x, weight, eps)
-        ctx.save_for_backward(x, weight, rstd)
-        return y
+    def apply(x, weight, eps):
+        return _ext().rmsnorm(x, weight, float(eps))
+
+
+class FusedAddRMSNormFunction:
+    """fused_add_rmsnorm's autograd node (C++): residual_out = x + residual
+    (one rounding), out = rmsnorm(residual_out); returns (out, residual_out).
+    Its backward takes the gradients of both outputs and returns one
+    gradient for x and residual."""
 
     @staticmethod
-    def backward(ctx, dy):
-        x, weight, rstd = ctx.saved_tensors
-        dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
-        dx, dgamma_f32, dgamma = _bwd_saved("rmsnorm_bwd", x, weight, _rows(dy), None, rstd, dgamma)
-        return dx, _weight_grad(dgamma_f32, dgamma, weight), None
+    def apply(x, residual, weight, eps):
+        return _ext().fused_add_rmsnorm(x, residual, weight, float(eps))
 
 
-class FusedAddRMSNormFunction(torch.autograd.Function):
-    """residual_out = x + residual (one rounding), out = rmsnorm(residual_out)."""
+class LayerNormFunction:
+    """layer_norm's autograd node (C++): y = (x - mean) * rstd * weight + bias
+    over the last dimension; the forward saves the fp32 mean and rstd."""
 
     @staticmethod
-    def forward(ctx, x, residual, weight, eps):
-        x = _rows(x)
-        residual = _rows(residual)
-        weight = weight.contiguous()
-        out, residual_out, rstd = fused_add_rmsnorm_fwd_rstd(x, residual, weight, eps)
-        ctx.save_for_backward(residual_out, weight, rstd)
-        return out, residual_out
-
-    @staticmethod
-    def backward(ctx, dout, dresidual_out):
-        added, weight, rstd = ctx.saved_tensors
-        if dout is None:
-            dout = torch.zeros_like(added)
-        dres = None if dresidual_out is None else _rows(dresidual_out)
-        dgamma = None if weight.dtype == torch.float32 else torch.empty_like(weight)
-        dx, dgamma_f32, dgamma = _bwd_saved("fused_add_rmsnorm_bwd", added, weight, _rows(dout), dres,
-                                            rstd, dgamma)
-        # x and residual enter only through their sum: one gradient for both
-        return dx, dx, _weight_grad(dgamma_f32, dgamma, weight), None
+    def apply(x, weight, bias, eps):
+        return _ext().layer_norm(x, weight, bias, float(eps))
 
 
 def rmsnorm(x, weight, eps=1e-6):
-    """Differentiable RMSNorm over the last dimension of x (any rank)."""
+    """Differentiable RMSNorm over the last dimension of x (any rank). Row
+    tensors the library can read in place (rows of unit stride under one row
+    stride) are not copied; others are made contiguous."""
     if x.shape[-1] != weight.numel():
         raise ValueError(f"rmsnorm: x.shape[-1]={x.shape[-1]} != weight length {weight.numel()}")
     return RMSNormFunction.apply(x, weight, eps)
@@ -106,33 +91,6 @@ def fused_add_rmsnorm(x, residual, weight, eps=1e-6, prenorm=True):
         raise ValueError(f"fused_add_rmsnorm: x.shape[-1]={x.shape[-1]} != weight length {weight.numel()}")
     out, residual_out = FusedAddRMSNormFunction.apply(x, residual, weight, eps)
     return (out, residual_out) if prenorm else out
-
-
-class LayerNormFunction(torch.autograd.Function):
-    """y = (x - mean) * rstd * weight + bias over the last dimension."""
-
-    @staticmethod
-    def forward(ctx, x, weight, bias, eps):
-        x = _rows(x)
-        weight = weight.contiguous()
-        bias = None if bias is None else bias.contiguous()
-        y, mean, rstd = layernorm_fwd_stats(x, weight, bias, eps)
-        ctx.save_for_backward(x, weight, mean, rstd)
-        ctx.has_bias = bias is not None
-        return y
-
-    @staticmethod
-    def backward(ctx, dy):
-        x, weight, mean, rstd = ctx.saved_tensors
-        half = weight.dtype != torch.float32
-        dgamma = torch.empty_like(weight) if half else None
-        dbeta = torch.empty_like(weight) if half and ctx.has_bias else None
-        dx, dg32, db32, dgamma, dbeta = layernorm_bwd(x, weight, _rows(dy), mean, rstd,
-                                                      dgamma=dgamma, dbeta=dbeta)
-        dbias = None
-        if ctx.has_bias:
-            dbias = db32 if not half else dbeta
-        return dx, _weight_grad(dg32, dgamma, weight), dbias, None
 
 
 def layer_norm(x, weight, bias=None, eps=1e-5):

@@ -40,7 +40,6 @@ int check_eps(float eps) {
 
 int check_flags(unsigned flags) {
     if (flags & ~7u) return RMSN_ERR_FLAGS;
-    if ((flags & 3u) == 3u) return RMSN_ERR_FLAGS;  // deterministic and atomic at once
     return RMSN_OK;
 }
 
@@ -90,19 +89,14 @@ int check_device(std::initializer_list<const void *> ptrs) {
     return RMSN_OK;
 }
 
-// dgamma mode actually run: a single block writes dgamma itself; otherwise
-// the requested mode, with AUTO resolving to the deterministic two-stage sum.
-int resolve_mode(unsigned flags, int64_t grid) {
-    if (grid <= 1) return rmsn::DG_DIRECT;
-    if ((flags & 3u) == RMSN_DGAMMA_ATOMIC) return rmsn::DG_ATOMIC;
-    return rmsn::DG_PARTIAL;
-}
+static_assert(rmsn::DM_AUTO == RMSN_DGAMMA_AUTO && rmsn::DM_DETERMINISTIC == RMSN_DGAMMA_DETERMINISTIC &&
+                  rmsn::DM_ATOMIC == RMSN_DGAMMA_ATOMIC && rmsn::DM_ONE_BLOCK == RMSN_DGAMMA_ONE_BLOCK,
+              "dgamma mode values");
 
 size_t workspace_for(int64_t M, int64_t N, int dtype, unsigned flags, bool vector_ok, int narrays) {
     RowPlan p;
     if (!rmsn::plan_rows(N, esize(dtype), vector_ok, &p)) return 0;
-    int64_t grid = rmsn::bwd_blocks(M, N, p);
-    return rmsn::bwd_workspace(M, N, p, resolve_mode(flags, grid), narrays);
+    return rmsn::bwd_workspace(M, N, p, flags & 3u, narrays);
 }
 
 // The public workspace query: alignment is not known here, so it answers for
@@ -138,8 +132,8 @@ int bwd_common(const void *x, int64_t ldx, const void *gamma, const void *dy, in
         aligned(gamma, 16) && rows_vector_ok({{x, ldx}, {dy, lddy}, {dres, lddres}, {dx, lddx}}, es);
     RowPlan p;
     if (!rmsn::plan_rows(N, es, vector_ok, &p)) return RMSN_ERR_SHAPE;
-    const int64_t grid = rmsn::bwd_blocks(M, N, p, !layer && dres != nullptr);
-    const int mode = resolve_mode(flags, grid);
+    const int64_t grid = rmsn::bwd_blocks(M, N, p, !layer && dres != nullptr, flags & 3u);
+    const int mode = rmsn::resolve_mode(flags & 3u, grid);
     // the public query's answer, whatever plan the pointers select, so a
     // buffer sized by the query is always accepted and nothing less is
     if (workspace_bytes < workspace_query(M, N, dtype, flags, layer ? 2 : 1)) return RMSN_ERR_WORKSPACE;
@@ -351,7 +345,7 @@ const char *rmsn_status_string(int status) {
     case RMSN_ERR_DTYPE: return "unknown dtype";
     case RMSN_ERR_EPS: return "eps must be finite and >= 0";
     case RMSN_ERR_WORKSPACE: return "workspace missing or too small";
-    case RMSN_ERR_FLAGS: return "unknown or contradictory flags";
+    case RMSN_ERR_FLAGS: return "unknown flags";
     case RMSN_ERR_DEVICE: return "pointer is not on the current device";
     case RMSN_ERR_HIP: return "HIP runtime error";
     case RMSN_ERR_ALIGN: return "pointer not aligned to its element size";

@@ -195,6 +195,35 @@ __device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, AUX_DEFAULT);
 }
 
+// ---------------------------------------------------------------------------
+// Row windows: a window is the RPB consecutive rows one block handles in a
+// step, one per row group.
+// ---------------------------------------------------------------------------
+// Byte address of element `elem` of a tensor, as an integer: window bases may
+// lie past the end of a tensor when the window holds no row (its descriptor
+// range is then empty and nothing is accessed).
+__device__ __forceinline__ const void *at(const void *base, int64_t elem, int es) {
+    return reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(base) + (uintptr_t)(elem * es));
+}
+
+// Buffer descriptor for one window of a row tensor with row stride ld
+// elements: rows wb .. wb + nr - 1 exist, and the range ends at the end of the
+// last of them, so rows past M, chunks past N and the gap between strided rows
+// all fall outside it.
+template <int ES>
+__device__ __forceinline__ rsrc_t window_rsrc(const void *base, int64_t wb, int64_t ld, uint32_t nr,
+                                              uint32_t row_bytes) {
+    const uint32_t span = nr == 0 ? 0u : (uint32_t)((int64_t)(nr - 1) * ld * ES) + row_bytes;
+    return make_rsrc(at(base, wb * ld, ES), span);
+}
+
+// Rows of the window starting at row wb that exist: min(RPB, M - wb), >= 0.
+template <int RPB>
+__device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
+    const int64_t r = M - wb;
+    return r <= 0 ? 0u : (r >= RPB ? (uint32_t)RPB : (uint32_t)r);
+}
+
 template <int DT, int VEC>
 __device__ __forceinline__ Pack<DT, VEC> zero_pack() {
     Pack<DT, VEC> p;

@@ -92,13 +92,6 @@ __device__ __forceinline__ void row_sum2(float &u, float &v, float *slots, int p
     }
 }
 
-// Byte address of element `elem` of a tensor, as an integer: window bases may
-// lie past the end of a tensor when the window holds no row (its descriptor
-// range is then empty and nothing is accessed).
-__device__ __forceinline__ const void *at(const void *base, int64_t elem, int es) {
-    return reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(base) + (uintptr_t)(elem * es));
-}
-
 // Store of a dgamma partial: plain (the default), so that the partials stay
 // in the caches for the finalize that reads them right after, or
 // non-temporal with RMSN_PARTIAL_NT. Measured on MI355X: plain stores take
@@ -115,26 +108,8 @@ __device__ __forceinline__ void partial_store(V v, V *p) {
 #endif
 }
 
-// Buffer descriptor for one window of a row tensor with row stride ld
-// elements: rows wb .. wb + nr - 1 exist, and the range ends at the end of the
-// last of them, so rows past M, chunks past N and the gap between strided rows
-// all fall outside it.
-template <int ES>
-__device__ __forceinline__ rsrc_t window_rsrc(const void *base, int64_t wb, int64_t ld, uint32_t nr,
-                                              uint32_t row_bytes) {
-    const uint32_t span = nr == 0 ? 0u : (uint32_t)((int64_t)(nr - 1) * ld * ES) + row_bytes;
-    return make_rsrc(at(base, wb * ld, ES), span);
-}
-
 // The operation a row kernel instance computes.
 enum : int { OP_RMS = 0, OP_RMS_FUSED = 1, OP_LN = 2 };
-
-// Rows of the window starting at row wb that exist: min(RPB, M - wb), >= 0.
-template <int RPB>
-__device__ __forceinline__ uint32_t rows_in(int64_t wb, int64_t M) {
-    const int64_t r = M - wb;
-    return r <= 0 ? 0u : (r >= RPB ? (uint32_t)RPB : (uint32_t)r);
-}
 
 // ---------------------------------------------------------------------------
 // Backward, main pass. [I769] Implementation plan, Math; [P800] PR-1 and

@@ -125,14 +125,24 @@ constexpr int BWD_MAX_BLOCKS = RMSN_BWD_MAX_BLOCKS;
 static_assert(RMSN_FUSED_MAX_BLOCKS <= RMSN_BWD_MAX_BLOCKS, "the workspace query assumes the larger grid");
 constexpr size_t WS_HEADER = 256;
 
+// The dgamma mode a caller asks for (the low two flag bits of the C ABI):
+// the measured default, the two-stage fixed-order sum, fp32 atomics, or one
+// block writing the gradients itself.
+enum : unsigned { DM_AUTO = 0, DM_DETERMINISTIC = 1, DM_ATOMIC = 2, DM_ONE_BLOCK = 3 };
+
 // Blocks the backward launches for M rows: one block per rpb rows at small M,
-// capped so each block folds many rows into one dgamma partial. A problem of
-// short rows (N <= 1024) and at most 8192 elements runs in one block that
-// writes the gradients itself, saving the finalize launch: measured on
-// MI355X (kernel time, HIP-graph replay) that is 6.2 instead of 7.7 us at
-// 32 x 256 bf16 and 4.2 instead of 5.6 us at 8 x 1024, while one block
-// holding several long rows is latency-bound (64 x 4096 bf16: 39.6 us against
-// 5.4 us with 64 blocks and partials).
+// capped so each block folds many rows into one dgamma partial. In the
+// default mode a problem of short rows (N <= 1024) and at most 8192 elements,
+// or of at most two rows of up to 8192 elements, runs in one block that
+// writes the gradients itself, saving the finalize launch; DM_ONE_BLOCK asks
+// for that at any size, and the two explicit cross-block modes never take it.
+// Measured on MI355X (GPU time per call from HIP-graph replay, median of
+// three, one block against the two-stage sum at the same shape), bf16:
+// 32 x 256 4.8 vs 6.6 us, 8 x 1024 4.8 vs 6.3, 2 x 4096 4.0 vs 5.6,
+// 2 x 8192 4.8 vs 6.3 (fp32 2 x 8192 6.4 vs 6.8); but 128 x 256 8.1 vs 6.6,
+// 16 x 1024 6.6 vs 6.4, 8 x 4096 7.8 vs 5.7 and 2 x 16384 8.2 vs 7.9, where
+// one CU holding the rows is latency-bound (4 x 4096: 5.7 either way). The
+// fp32-atomic mode never beats the two-stage sum.
 //
 // A fused-add backward with a dresidual_out reads three row tensors; from
 // 4096 rows on it runs at most 192 blocks (RMSN_FUSED_MAX_BLOCKS,
@@ -141,8 +151,11 @@ constexpr size_t WS_HEADER = 256;
 // 8192 x 4096 48.6 -> 46.8 us, 4096 x 4096 27.6 -> 27.0 us; the plain and
 // LayerNorm backwards (two row reads) lose with fewer blocks, and so do
 // fused calls of fewer rows (1024 x 8192: 18.1 -> 19.4 us).
-inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool three_reads = false) {
-    if (M <= 0 || (N <= 1024 && M * N <= 8192)) return 1;
+inline bool one_block_rule(int64_t M, int64_t N) { return (N <= 1024 && M * N <= 8192) || (M <= 2 && N <= 8192); }
+
+inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool three_reads = false,
+                          unsigned dmode = DM_AUTO) {
+    if (M <= 0 || dmode == DM_ONE_BLOCK || (dmode == DM_AUTO && one_block_rule(M, N))) return 1;
     int64_t steps = (M + p.rpb - 1) / p.rpb;
     if (steps < 1) steps = 1;
     const int64_t cap = three_reads && M >= RMSN_FUSED_CAP_MIN_M ? RMSN_FUSED_MAX_BLOCKS : BWD_MAX_BLOCKS;
@@ -151,6 +164,15 @@ inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool three_rea
 
 // dgamma combining modes actually run.
 enum : int { DG_DIRECT = 0, DG_PARTIAL = 1, DG_ATOMIC = 2 };
+
+// What a call in mode dmode runs on `grid` blocks: one block writes dgamma
+// itself in the default and one-block modes; otherwise the requested
+// cross-block sum, the default resolving to the deterministic two-stage sum.
+inline int resolve_mode(unsigned dmode, int64_t grid) {
+    if (dmode == DM_ONE_BLOCK || (dmode == DM_AUTO && grid <= 1)) return DG_DIRECT;
+    if (dmode == DM_ATOMIC) return DG_ATOMIC;
+    return DG_PARTIAL;
+}
 
 // Block partials of dgamma are stored in tiles of FIN_TILE columns: tile t
 // holds, for every block g, the block's partials of columns
@@ -166,15 +188,16 @@ constexpr int64_t partial_index(int64_t col, int64_t block, int64_t G) {
     return (col / FIN_TILE) * G * FIN_TILE + block * FIN_TILE + col % FIN_TILE;
 }
 
-// Bytes of workspace for a backward call: a header, then the tiled fp32 block
-// partials, one array per weight gradient (narrays: 1 for RMSNorm's dgamma,
-// 2 for LayerNorm's dgamma and dbeta), when they are combined by the
-// fixed-order kernel.
-inline size_t bwd_workspace(int64_t M, int64_t N, const RowPlan &p, int mode, int narrays = 1) {
+// Bytes of workspace for a backward call in mode dmode: a header, then the
+// tiled fp32 block partials, one array per weight gradient (narrays: 1 for
+// RMSNorm's dgamma, 2 for LayerNorm's dgamma and dbeta), when they are
+// combined by the fixed-order kernel. Sized for the larger (two-read) grid.
+inline size_t bwd_workspace(int64_t M, int64_t N, const RowPlan &p, unsigned dmode, int narrays = 1) {
     size_t ws = WS_HEADER;
-    if (mode == DG_PARTIAL) {
+    const int64_t G = bwd_blocks(M, N, p, false, dmode);
+    if (resolve_mode(dmode, G) == DG_PARTIAL) {
         const int64_t tiles = (N + FIN_TILE - 1) / FIN_TILE;
-        ws += (size_t)narrays * (size_t)bwd_blocks(M, N, p) * (size_t)(tiles * FIN_TILE) * sizeof(float);
+        ws += (size_t)narrays * (size_t)G * (size_t)(tiles * FIN_TILE) * sizeof(float);
     }
     return ws;
 }

@@ -57,15 +57,19 @@ int main() {
                     // workspace query sizes for
                     const int64_t G3 = bwd_blocks(M, N, p, true);
                     CHECK(G3 >= 1 && G3 <= G, "fused grid %lld above %lld", (long long)G3, (long long)G);
-                    for (int mode : {DG_DIRECT, DG_PARTIAL, DG_ATOMIC})
+                    for (unsigned dm : {DM_AUTO, DM_DETERMINISTIC, DM_ATOMIC, DM_ONE_BLOCK})
                         for (int na : {1, 2}) {
-                            const size_t ws = bwd_workspace(M, N, p, mode, na);
+                            const size_t ws = bwd_workspace(M, N, p, dm, na);
                             CHECK(ws >= WS_HEADER, "workspace below its header");
-                            if (mode != DG_PARTIAL) continue;
+                            const int64_t Gm = bwd_blocks(M, N, p, false, dm);
+                            CHECK(dm != DM_ONE_BLOCK || Gm == 1, "one-block mode on %lld blocks", (long long)Gm);
+                            CHECK(dm != DM_AUTO || Gm == G, "default grid differs");
+                            CHECK(bwd_blocks(M, N, p, true, dm) <= Gm, "fused grid above the sized one");
+                            if (resolve_mode(dm, Gm) != DG_PARTIAL) continue;
                             // the last partial of every array lies inside the workspace
                             const int64_t tiles = (N + FIN_TILE - 1) / FIN_TILE;
-                            const int64_t pstride = tiles * FIN_TILE * G;
-                            const int64_t last = (na - 1) * pstride + partial_index(N - 1, G - 1, G);
+                            const int64_t pstride = tiles * FIN_TILE * Gm;
+                            const int64_t last = (na - 1) * pstride + partial_index(N - 1, Gm - 1, Gm);
                             CHECK((size_t)(last + 1) * sizeof(float) + WS_HEADER <= ws,
                                   "partial index %lld past a workspace of %zu bytes", (long long)last, ws);
                             // the header bound the C header states for the default tile

@@ -112,7 +112,7 @@ BWD_CASES = [
     ("M < 0", dict(M=-1), SHAPE),
     ("M too large", dict(M=1 << 31), SHAPE),
     ("unknown flag", dict(flags=8), FLAGS),
-    ("both dgamma modes", dict(flags=3), FLAGS),
+    ("unknown high flag", dict(flags=16), FLAGS),
     ("gamma NULL", dict(gamma=None), NULL),
     ("dgamma_f32 NULL", dict(dg32=None), NULL),
     ("workspace NULL", dict(ws=None), NULL),
@@ -151,13 +151,17 @@ def test_layernorm_bwd_validation_of_its_own_operands():
 
 def test_small_short_row_problems_run_in_one_block():
     """The default mode's measured rule: rows of at most 1024 elements and at
-    most 8192 elements in all run in one block that writes dgamma itself (no
-    partials); anything larger uses per-block partials."""
+    most 8192 elements in all, or at most two rows of up to 8192 elements,
+    run in one block that writes dgamma itself (no partials); anything
+    larger uses per-block partials. The explicit modes ignore the rule."""
     q = R.rmsnorm_bwd_workspace_bytes
-    for M, N in ((32, 256), (8, 1024), (1, 4096), (1, 16384), (64, 128)):
+    for M, N in ((32, 256), (8, 1024), (1, 4096), (1, 16384), (64, 128), (2, 4096), (2, 8192)):
         assert q(M, N, R.BF16) == 256, (M, N)
-    for M, N in ((33, 256), (9, 1024), (2, 4096), (5, 2048)):
+        assert q(M, N, R.BF16, R.DGAMMA_ONE_BLOCK) == 256, (M, N)
+        assert q(M, N, R.BF16, R.DGAMMA_DETERMINISTIC) > 256, (M, N)
+    for M, N in ((33, 256), (9, 1024), (3, 4096), (5, 2048), (2, 16384), (2, 8200)):
         assert q(M, N, R.BF16) > 256, (M, N)
+        assert q(M, N, R.BF16, R.DGAMMA_ONE_BLOCK) == 256, (M, N)
 
 
 def test_layernorm_workspace_holds_two_partial_arrays():
@@ -239,8 +243,12 @@ def test_fwd_with_no_rows_is_ok_without_a_launch():
 def test_workspace_query():
     q = R.rmsnorm_bwd_workspace_bytes
     assert q(4, 0, R.BF16) == 0 and q(4, 64, 9) == 0 and q(-1, 64, R.BF16) == 0
-    assert q(4, 64, R.BF16, flags=3) == 0
-    # a single block writes dgamma itself: header only
+    assert q(4, 64, R.BF16, flags=8) == 0
+    # a single block writes dgamma itself: header only (the one-block mode at
+    # any size)
+    assert q(4096, 4096, R.BF16, R.DGAMMA_ONE_BLOCK) == 256
+    # the deterministic mode always uses partials, a single block's included
+    assert q(1, 4096, R.BF16, R.DGAMMA_DETERMINISTIC) == 256 + 4096 * 4
     assert q(1, 4096, R.BF16) == 256
     assert q(0, 4096, R.BF16) == 256
     # many rows: one fp32 partial row per block (at most 256 blocks), in the
@@ -346,4 +354,4 @@ def test_no_alloc_refuses_before_any_hip_call():
     assert no_alloc(N=R.MAX_N + 1) == SHAPE
     assert no_alloc(M=-1) == SHAPE
     assert no_alloc(flags=8) == FLAGS
-    assert no_alloc(flags=3) == FLAGS
+    assert no_alloc(flags=16) == FLAGS

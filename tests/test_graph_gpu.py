@@ -166,8 +166,13 @@ def test_captured_autograd_backward_keeps_its_own_workspace():
     torch.cuda.synchronize()
     xb, dyb = draw(62, M_big, N, dt).to(DEV), draw(63, M_big, N, dt, 0.0, 1e-2).to(DEV)
     with torch.cuda.stream(cap):
+        # larger calls replace both caches of stream `cap`: the binding's and
+        # the autograd nodes'
         _, rb = R.rmsnorm_fwd_rstd(xb, w.detach(), eps)
-        R.rmsnorm_bwd(xb, w.detach(), dyb, rb)  # replaces the cached workspace
+        R.rmsnorm_bwd(xb, w.detach(), dyb, rb)
+        xbg = xb.clone().requires_grad_()
+        torch.autograd.grad(R.rmsnorm(xbg, w, eps), (xbg, w), dyb)
+        del xbg
         junk = [torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV) for _ in range(4)]
     torch.cuda.synchronize()
     for i in range(REPLAYS):

@@ -110,8 +110,10 @@ EDGE = [
     (300, 64, "bf16"), (1000, 128, "f32"), (129, 1024, "f16"), (64, 2048, "f16"),
     (33, 8192, "bf16"), (17, 16384, "bf16"), (6, 16384, "f32"), (2, 12288, "f32"),
     (1, 16383, "bf16"), (700, 768, "bf16"), (258, 5120, "f16"),
-    # both sides of the one-block rule (N <= 1024 and M * N <= 8192)
+    # both sides of the one-block rule (N <= 1024 and M * N <= 8192, or
+    # M <= 2 and N <= 8192)
     (32, 256, "bf16"), (33, 256, "bf16"), (8, 1024, "f32"), (9, 1024, "f32"),
+    (2, 8192, "bf16"), (3, 4096, "bf16"), (2, 16384, "f32"), (2, 3000, "f32"),
     # a few blocks fill their window ring (and pause in the prologue) while
     # the rest hold fewer windows: 517 or 515 windows over 256 blocks
     (517, 4096, "bf16"), (1029, 2048, "bf16"), (517, 8192, "bf16"),
@@ -310,6 +312,30 @@ def test_deterministic_mode_repeats_bit_for_bit(name):
 def test_atomic_mode_within_tolerance(name):
     _say("case atomic", name)
     check_case(plain_case(W[name], flags=R.DGAMMA_ATOMIC))
+
+
+@pytest.mark.parametrize("M,N,dt", [(1, 4096, "bf16"), (64, 2048, "bf16"), (300, 3000, "f32"),
+                                     (33, 256, "f16"), (5, 1001, "bf16")])
+def test_one_block_mode_at_any_size(M, N, dt):
+    """The explicit one-block mode: one workgroup walks every row and writes
+    the gradients itself, also where the default would use many blocks."""
+    _say("case one-block mode", M, N, dt)
+    check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-5, seed=M * 7 + N), flags=R.DGAMMA_ONE_BLOCK))
+    check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M * 5 + N), flags=R.DGAMMA_ONE_BLOCK))
+
+
+@pytest.mark.parametrize("M,N,dt", [(1, 4096, "bf16"), (8, 1024, "f32"), (32, 256, "bf16"), (3, 7, "f16")])
+def test_deterministic_mode_where_the_default_runs_one_block(M, N, dt):
+    """The explicit deterministic mode keeps its two-stage sum (block
+    partials, then the fixed-order finalize) on problems the default runs
+    in one block, and repeats bit for bit."""
+    _say("case deterministic at one-block shapes", M, N, dt)
+    c = plain_case(workloads.custom("plain", M, N, dt, 1e-5, seed=N + 3), flags=R.DGAMMA_DETERMINISTIC)
+    check_case(c)
+    xg, gg, dyg, rg = c["inputs"]
+    dx, dg32, _ = R.rmsnorm_bwd(xg, gg, dyg, rg, flags=R.DGAMMA_DETERMINISTIC)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, c["dx"][0]) and torch.equal(dg32, c["dg32"][0])
 
 
 def test_atomic_mode_fused():
