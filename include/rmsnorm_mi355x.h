@@ -39,7 +39,10 @@
  *   - Arguments are validated before anything is enqueued; a rejected call
  *     writes nothing. Inputs and outputs must not overlap, except where an
  *     entry point says so.
- *   - Limits: 0 <= M <= 2^31 - 1, 1 <= N <= RMSN_MAX_N.
+ *   - Limits: 0 <= M <= 2^31 - 1, 1 <= N <= RMSN_MAX_N. Rows of up to 16384
+ *     elements stay in registers between the passes over them; longer rows
+ *     are read once by the forwards and twice by the backwards (the second
+ *     read mostly from the caches), with identical results.
  */
 #ifndef RMSNORM_MI355X_H
 #define RMSNORM_MI355X_H
@@ -51,7 +54,7 @@
 extern "C" {
 #endif
 
-#define RMSN_MAX_N 16384
+#define RMSN_MAX_N 32768
 /* Largest row stride, in elements, of the *_strided entry points. */
 #define RMSN_MAX_LD (1LL << 24)
 

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "librmsnorm_mi355x.so")
 
 F32, F16, BF16 = 0, 1, 2
 DGAMMA_AUTO, DGAMMA_DETERMINISTIC, DGAMMA_ATOMIC, DGAMMA_ONE_BLOCK, CHECK_DEVICE = 0, 1, 2, 3, 4
-MAX_N = 16384
+MAX_N = 32768
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 _lib = None

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librmsnorm_mi355x.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "capi.cpp")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "long_rows.hip"), os.path.join(CSRC, "capi.cpp")]
 FLOOR_LIB = os.path.join(HERE, "libstream_floor.so")
 FLOOR_SOURCES = [os.path.join(CSRC, "stream_floor.hip")]
 

@@ -919,11 +919,13 @@ template <int DT, int VEC, int TPR, int K> struct FwdLaunch {
 
 template <int DT>
 static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s) {
+    if (p.long_row) return launch_bwd_long(DT, p, a, grid, s);
     return dispatch<BwdLaunch, DT>(p, a, grid, s);
 }
 
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
+    if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
     return dispatch<FwdLaunch, DT>(p, a, grid, s);
 }
 

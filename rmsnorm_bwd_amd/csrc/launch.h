@@ -55,4 +55,9 @@ hipError_t device_scratch(void **ptr);
 // Enqueue the forward on stream s with `grid` blocks.
 hipError_t launch_fwd(int dtype, const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s);
 
+// The main pass of the backward, and the forward, for long rows
+// (p.long_row): long_rows.hip.
+hipError_t launch_bwd_long(int dtype, const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s);
+hipError_t launch_fwd_long(int dtype, const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s);
+
 }  // namespace rmsn

@@ -20,6 +20,7 @@ struct RowPlan {
     int k;      // chunks per thread
     int block;  // threads per block
     int rpb;    // rows per block per step
+    bool long_row;  // a row of more than LONG_N elements: the two-pass kernels of long_rows.hip
 };
 
 inline int pow2_ceil(int64_t v) {
@@ -68,8 +69,10 @@ constexpr int block_threads(int tpr) {
     return tpr <= 64 ? RMSN_BLOCK_WAVE : (tpr > RMSN_BLOCK_MIN ? tpr : RMSN_BLOCK_MIN);
 }
 
-// Largest supported row length.
-constexpr int64_t MAX_N = 16384;
+// Largest supported row length, and the longest row the register-resident
+// window ring takes (longer rows: 512 threads a row, 64 elements a thread).
+constexpr int64_t MAX_N = 32768;
+constexpr int64_t LONG_N = 16384;
 
 // Choose the row plan for N elements of esize bytes. vector_ok says every
 // row-tensor pointer and gamma are 16-byte aligned; the vector path also needs
@@ -77,10 +80,21 @@ constexpr int64_t MAX_N = 16384;
 // Longer rows take more chunks per thread rather than more threads: a row
 // spreads over at most 512 threads, so a thread holds up to 32 elements of a
 // 16384-element row, and every block has at most 512 threads (whose waves
-// may use 256 VGPRs). Returns false when N is out of range.
+// may use 256 VGPRs). Rows of more than LONG_N elements take the long-row
+// kernels: 512 threads a row, 64 elements a thread (vector chunks or single
+// elements). Returns false when N is out of range.
 inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
     if (N < 1 || N > MAX_N) return false;
     const int vw = 16 / esize;
+    p->long_row = N > LONG_N;
+    if (p->long_row) {
+        p->vec = vector_ok && N % vw == 0 ? vw : 1;
+        p->k = 64 / p->vec;
+        p->tpr = 512;
+        p->block = 512;
+        p->rpb = 1;
+        return true;
+    }
     if (vector_ok && N % vw == 0) {
         const int64_t C = N / vw;  // vector chunks per row
         p->vec = vw;

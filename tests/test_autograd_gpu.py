@@ -133,3 +133,29 @@ def test_fused_add_autograd_with_only_residual_out_in_the_loss():
     assert torch.equal(xg.grad.cpu(), g2)
     assert torch.equal(rg.grad.cpu(), g2)
     assert torch.count_nonzero(wg.grad).item() == 0
+
+
+def test_autograd_long_rows():
+    """rmsnorm and fused_add_rmsnorm through autograd on rows longer than
+    16384 elements (the two-pass kernels), against the oracle."""
+    print("case autograd long rows (2, 3, 20000) bf16", flush=True)
+    shape, N, eps = (2, 3, 20000), 20000, 1e-6
+    x, res = _draw(shape, 21), _draw(shape, 22)
+    w = _draw((N,), 23, 1.0, 0.1)
+    g, gr = _draw(shape, 24, 0.0, 1e-2), _draw(shape, 25, 0.0, 1e-2)
+    xg, wg = x.to(DEV).requires_grad_(), w.to(DEV).requires_grad_()
+    R.rmsnorm(xg, wg, eps).backward(g.to(DEV))
+    xf, rf, wf = x.to(DEV).requires_grad_(), res.to(DEV).requires_grad_(), w.to(DEV).requires_grad_()
+    out, res_out = R.fused_add_rmsnorm(xf, rf, wf, eps)
+    torch.autograd.backward((out, res_out), (g.to(DEV), gr.to(DEV)))
+    torch.cuda.synchronize()
+    x2, r2 = x.reshape(-1, N), res.reshape(-1, N)
+    rs, _ = oracle.rmsnorm_fwd(x2, w, eps)
+    dx_ref, dg_ref = oracle.rmsnorm_bwd(x2, w, g.reshape(-1, N), rs)
+    assert_close("dx", xg.grad.reshape(-1, N), dx_ref, torch.bfloat16)
+    assert_close("dweight", wg.grad, dg_ref, torch.bfloat16)
+    a_ref, ra, _ = oracle.fused_add_rmsnorm_fwd(x2, r2, w, eps)
+    dxf_ref, dgf_ref = oracle.fused_add_rmsnorm_bwd(a_ref, w, g.reshape(-1, N), gr.reshape(-1, N), ra)
+    assert torch.equal(xf.grad, rf.grad)
+    assert_close("fused dx", xf.grad.reshape(-1, N), dxf_ref, torch.bfloat16)
+    assert_close("fused dweight", wf.grad, dgf_ref, torch.bfloat16)

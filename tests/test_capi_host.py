@@ -170,7 +170,7 @@ def test_layernorm_workspace_holds_two_partial_arrays():
     assert ql(4096, 4096, R.BF16, R.DGAMMA_ATOMIC) == 256
     assert ql(1, 4096, R.BF16) == 256
     for M in (1, 7, 5000):
-        for N in (1, 255, 4096, 16384):
+        for N in (1, 255, 4096, 16384, 32768):
             assert ql(M, N, R.F32) - 256 == 2 * (q(M, N, R.F32) - 256)
     assert ql(4, 0, R.BF16) == 0 and ql(4, 64, 9) == 0
 
@@ -257,7 +257,7 @@ def test_workspace_query():
     assert q(4096, 4096, R.BF16, R.DGAMMA_DETERMINISTIC) == 256 + 256 * 4096 * 4
     assert q(4096, 4096, R.BF16, R.DGAMMA_ATOMIC) == 256
     for M in (1, 7, 100, 5000, 1 << 20):
-        for N in (1, 3, 255, 3000, 4096, 16384):
+        for N in (1, 3, 255, 3000, 4096, 16384, 16385, 20000, 32768):
             for dt in (R.F32, R.F16, R.BF16):
                 v = q(M, N, dt)
                 assert 256 <= v <= 256 + 256 * (-(-N // 16) * 16) * 4

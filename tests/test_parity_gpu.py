@@ -143,6 +143,53 @@ def test_fused_short_rows_at_large_M():
     check_case(fused_case(workloads.custom("fused", 131075, 128, "bf16", 1e-6, seed=7)))
 
 
+# Rows longer than 16384 elements: the two-pass long-row kernels (16-byte
+# chunks where N and the pointers allow, single elements otherwise), one row
+# per block of 512 threads; 257 rows put two rows on one block of 256.
+LONG = [(3, 16385, "bf16"), (5, 20000, "f32"), (130, 32768, "bf16"), (7, 32768, "f32"),
+        (9, 30001, "f16"), (257, 24576, "bf16"), (1, 32768, "f16"), (2, 20480, "bf16")]
+
+
+@pytest.mark.parametrize("M,N,dt", LONG)
+def test_long_rows(M, N, dt):
+    _say("case long rows", M, N, dt)
+    check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-5, seed=M + N)))
+    check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M + 3 * N)))
+
+
+@pytest.mark.parametrize("flags", [R.DGAMMA_DETERMINISTIC, R.DGAMMA_ATOMIC, R.DGAMMA_ONE_BLOCK])
+def test_long_rows_every_dgamma_mode(flags):
+    _say("case long rows, mode", flags)
+    check_case(plain_case(workloads.custom("plain", 40, 24576, "bf16", 1e-5, seed=11), flags=flags))
+    check_case(fused_case(workloads.custom("fused", 33, 20000, "f32", 1e-6, seed=12), flags=flags))
+
+
+def test_long_rows_misaligned_and_in_place():
+    _say("case long rows misaligned, in-place residual_out")
+    check_case(plain_case(workloads.custom("plain", 4, 20000, "bf16", 1e-5), misalign=True))
+    check_case(fused_case(workloads.custom("fused", 3, 18000, "f16", 1e-5), misalign=True))
+    w = workloads.custom("fused", 6, 25000, "bf16", 1e-6)
+    d = workloads.make_inputs(w)
+    a_ref, r_ref, o_ref = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps)
+    res = d["residual"].to(DEV)
+    out, res_out, rstd = R.fused_add_rmsnorm_fwd_rstd(d["x"].to(DEV), res, d["gamma"].to(DEV), w.eps,
+                                                      residual_out=res)
+    torch.cuda.synchronize()
+    assert torch.equal(res.cpu(), a_ref)
+    assert_close("out", out, o_ref, torch.bfloat16)
+
+
+def test_long_rows_deterministic_repeats_bit_for_bit():
+    _say("case long rows deterministic repeat")
+    c = plain_case(workloads.custom("plain", 300, 32768, "bf16", 1e-6, seed=5), flags=R.DGAMMA_DETERMINISTIC)
+    check_case(c)
+    xg, gg, dyg, rg = c["inputs"]
+    for _ in range(2):
+        dx, dg32, _ = R.rmsnorm_bwd(xg, gg, dyg, rg, flags=R.DGAMMA_DETERMINISTIC)
+        torch.cuda.synchronize()
+        assert torch.equal(dx, c["dx"][0]) and torch.equal(dg32, c["dg32"][0])
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("k", [40, -40])
 @pytest.mark.parametrize("M,N", [(64, 4096), (7, 3001)])

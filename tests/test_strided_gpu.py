@@ -63,6 +63,8 @@ BWD_CASES = [
     ("64x8192_bf16_vec", 64, 8192, "bf16", (64, 8, 8, 8)),          # two chunks a thread
     ("77x1000_bf16_elem", 77, 1000, "bf16", (1, 3, 5, 2)),          # element path
     ("50x4096_f32_elem", 50, 4096, "f32", (1, 0, 3, 0)),            # element path (one odd stride)
+    ("20x20000_bf16_long_vec", 20, 20000, "bf16", (8, 16, 0, 8)),   # long rows, 16-byte chunks
+    ("9x24577_f32_long_elem", 9, 24577, "f32", (1, 2, 0, 3)),       # long rows, element path
 ]
 
 
