@@ -247,15 +247,15 @@ def mode_sweep(reps=3):
                 torch.cuda.empty_cache()
 
 
-def shape_sweep(steps=50):
+def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 4096, 16384, 32768)):
     """The backward and the forward of plain and fused-add RMSNorm (bf16) over
     an (M, N) grid: GPU time per call from one HIP-graph replay of `steps`
     calls rotating over buffer sets of > 512 MiB (as the headline is timed),
     algorithmic GB/s and its share of 8 TB/s. One JSON line per shape."""
     dev = torch.device("cuda:0")
     for op in ("plain", "fused"):
-        for N in (1024, 2048, 4096, 8192):
-            for M in (1, 128, 512, 1024, 4096, 16384, 32768):
+        for N in ns:
+            for M in ms:
                 w = workloads.custom(op, M, N, "bf16", 1e-6, dy_sigma=1e-2)
                 per = (4 if op == "fused" else 3) * M * N * 2
                 # a replay touches at most `steps` sets; below 512 MiB in all
@@ -609,6 +609,10 @@ def main():
     ap.add_argument("--shape-sweep", action="store_true",
                     help="time plain and fused backward and forward (bf16) on an (M, N) grid "
                          "(one JSON line per shape) and exit")
+    ap.add_argument("--sweep-n", default="1024,2048,4096,8192",
+                    help="row lengths of --shape-sweep (comma-separated)")
+    ap.add_argument("--sweep-m", default="1,128,512,1024,4096,16384,32768",
+                    help="row counts of --shape-sweep (comma-separated)")
     ap.add_argument("--api-compare", action="store_true",
                     help="time the backward through autograd against torch's eager RMSNorm on the "
                          "pages' public-API shapes (one JSON line per shape) and exit")
@@ -637,7 +641,8 @@ def main():
         api_compare()
         return
     if args.shape_sweep:
-        shape_sweep()
+        shape_sweep(ns=[int(v) for v in args.sweep_n.split(",")],
+                    ms=[int(v) for v in args.sweep_m.split(",")])
         return
     if args.floor:
         floor(workloads.WORKLOADS[args.workload])

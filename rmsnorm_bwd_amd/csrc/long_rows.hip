@@ -27,13 +27,17 @@
 // The fused forward's residual_out may be residual itself: nothing is read
 // after it is written.
 //
-// Backward: in registers the row (x and dy, and dresidual_out) would leave
-// too little room for the 64 (LayerNorm: 128) fp32 weight-gradient
-// accumulators, so the row is read twice: the first pass forms the row sums
-// (sum x*wdy; for LayerNorm also sum wdy), the second re-reads x, dy and
-// dresidual_out (mostly from the caches: a block re-reads what it read one
-// pass earlier), writes dx and folds dy * x_hat (and dy) into the
-// accumulators. gamma is re-read with the row (it stays in the caches).
+// Backward, RMSNorm (plain and fused): the row (x, dy, dresidual_out) stays
+// in registers and each thread's 64 fp32 weight-gradient accumulators live
+// in LDS (128 KiB a block: a thread's own slots, so no barrier guards them),
+// so each row is read once. gamma is read with the row (it stays in the
+// caches).
+//
+// Backward, LayerNorm: two accumulator arrays (dgamma, dbeta) would need
+// 256 KiB of LDS, so the row is read twice instead: the first pass forms the
+// row sums (sum (x - mean)*wdy and sum wdy), the second re-reads x and dy
+// (mostly from the caches: the block read them one pass earlier), writes dx
+// and folds dy * x_hat and dy into accumulators in registers.
 #include "device.h"
 #include "launch.h"
 #include "plan.h"
@@ -83,12 +87,10 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
     const int64_t M = a.M;
     const uint32_t row_bytes = (uint32_t)N * ES;
     const int nchunk = N / VEC;
-    uint32_t coff[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
+    auto off = [&](int k) -> uint32_t {
         const int c = threadIdx.x + k * LB;
-        coff[k] = c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
-    }
+        return c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
+    };
     const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
     const rsrc_t rb = make_rsrc(a.beta, LN && a.beta ? row_bytes : 0u);
     const float inv_n = 1.0f / (float)N;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
         const rsrc_t rx = window_rsrc<ES>(a.x, row, a.ldx, 1, row_bytes);
         P av[K];  // the row (for the fused variant, added = x + residual rounded)
 #pragma unroll
-        for (int k = 0; k < K; ++k) av[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, coff[k]);
+        for (int k = 0; k < K; ++k) av[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, off(k));
         if constexpr (FUSED) {
             const rsrc_t rr = window_rsrc<ES>(a.residual, row, a.ldres, 1, row_bytes);
             const rsrc_t ro = window_rsrc<ES>(a.residual_out, row, a.ldres_out, 1, row_bytes);
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
             for (int k0 = 0; k0 < K; k0 += LGROUP) {
                 P rv[LGROUP];
 #pragma unroll
-                for (int j = 0; j < LGROUP; ++j) rv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rr, coff[k0 + j]);
+                for (int j = 0; j < LGROUP; ++j) rv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rr, off(k0 + j));
 #pragma unroll
                 for (int j = 0; j < LGROUP; ++j) {
                     float t[VEC];
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
             // every residual read is done before residual_out (which may be
             // residual itself) is written
 #pragma unroll
-            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ro, coff[k], av[k]);
+            for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_STREAM_STORE>(ro, off(k), av[k]);
         }
         float r, mu = 0.f;
         if constexpr (LN) {
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float d = coff[k] == OOB ? 0.f : elem(av[k], e) - mu;  // chunks past the row end
+                    const float d = off(k) == OOB ? 0.f : elem(av[k], e) - mu;  // chunks past the row end
                     s2[0] = fmaf(d, d, s2[0]);
                 }
             block_sum<1>(s2, slots, parity);
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
             P gv[LGROUP], bv[LN ? LGROUP : 1];
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
-                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k0 + j]);
-                if constexpr (LN) bv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rb, coff[k0 + j]);
+                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+                if constexpr (LN) bv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rb, off(k0 + j));
             }
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
@@ -170,50 +172,181 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
                     else
                         o[e] = elem(av[k0 + j], e) * r * elem(gv[j], e);
                 }
-                buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(ry, coff[k0 + j],
+                buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(ry, off(k0 + j),
                                                                                make_pack<DT, VEC>(o));
             }
         }
     }
 }
 
+// One weight-gradient sum of this block for column j of array q (0 dgamma,
+// 1 dbeta): a partial (the two-stage sum), an fp32 atomic add, or, when one
+// block runs the call, the gradient itself and its dtype copy.
+template <int DT>
+__device__ __forceinline__ void emit_long(const BwdArgs &a, int q, int j, float v, int G, int64_t pstride) {
+    float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
+    void *outT = q ? a.dbeta : a.dgamma;
+    if (a.mode == DG_PARTIAL) {
+        a.partials[q * pstride + partial_index(j, blockIdx.x, G)] = v;
+    } else if (a.mode == DG_ATOMIC) {
+        unsafeAtomicAdd(out32 + j, v);
+    } else {
+        out32[j] = v;
+        if (outT) {
+            if constexpr (DT == DT_F32)
+                static_cast<float *>(outT)[j] = v;
+            else
+                static_cast<uint16_t *>(outT)[j] = pack1<DT>(v);
+        }
+    }
+}
+
+typedef float lf32x4 __attribute__((ext_vector_type(4)));
+constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread
+
 // ---------------------------------------------------------------------------
-// Backward, long rows: two passes over each row (see the file comment).
+// Backward, long rows, RMSNorm on 16-byte chunks: row in registers, one
+// read; the dgamma accumulators in LDS.
 // ---------------------------------------------------------------------------
 template <int DT, int VEC, int OP>
-__global__ __launch_bounds__(LB) void bwd_long_kernel(BwdArgs a) {
+__global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
+    using P = Pack<DT, VEC>;
+    constexpr int K = 64 / VEC;
+    constexpr bool FUSED = OP == OPL_FUSED;
+    constexpr int ES = ElemSize<DT>::value;
+    static_assert((LGROUP * VEC) % 4 == 0, "whole accumulator slots per group");
+    // slot s of thread t at acc_lds[s][t]: consecutive lanes, consecutive 16 bytes
+    __shared__ lf32x4 acc_lds[NSLOT][LB];
+    __shared__ float slots[2 * LWAVES];
+    const int N = a.N;
+    const int64_t M = a.M;
+    const int G = gridDim.x;
+    const int t = threadIdx.x;
+    const uint32_t row_bytes = (uint32_t)N * ES;
+    const int nchunk = N / VEC;
+    const float inv_n = 1.0f / (float)N;
+    auto off = [&](int k) -> uint32_t {
+        const int c = t + k * LB;
+        return c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
+    };
+#pragma unroll
+    for (int q = 0; q < NSLOT; ++q) acc_lds[q][t] = lf32x4{0.f, 0.f, 0.f, 0.f};
+    const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
+    int parity = 0;
+    for (int64_t row = blockIdx.x; row < M; row += G) {
+        const rsrc_t rx = window_rsrc<ES>(a.x, row, a.ldx, 1, row_bytes);
+        const rsrc_t rd = window_rsrc<ES>(a.dy, row, a.lddy, 1, row_bytes);
+        P xv[K], dv[K], zv[FUSED ? K : 1];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, off(k));
+            dv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, off(k));
+        }
+        if constexpr (FUSED) {
+            const rsrc_t rz = window_rsrc<ES>(a.dres, row, a.lddres, 1, row_bytes);
+#pragma unroll
+            for (int k = 0; k < K; ++k) zv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, off(k));
+        }
+        const float r = buf_load_f32(make_rsrc(at(a.rstd, row, 4), 4u), 0u);
+        float s[1] = {0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += LGROUP) {
+            P gv[LGROUP];
+#pragma unroll
+            for (int j = 0; j < LGROUP; ++j) gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+#pragma unroll
+            for (int j = 0; j < LGROUP; ++j)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    s[0] = fmaf(elem(xv[k0 + j], e), elem(dv[k0 + j], e) * elem(gv[j], e), s[0]);
+        }
+        block_sum<1>(s, slots, parity);
+        const float b = r * r * (s[0] * r * inv_n);  // r^2 c1, c1 = r sum x wdy / N
+        const rsrc_t rw = window_rsrc<ES>(a.dx, row, a.lddx, 1, row_bytes);
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += LGROUP) {
+            P gv[LGROUP];
+#pragma unroll
+            for (int j = 0; j < LGROUP; ++j) gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+            float tv[LGROUP * VEC];  // this group's dy * x_hat terms
+#pragma unroll
+            for (int j = 0; j < LGROUP; ++j) {
+                const int k = k0 + j;
+                float o[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float xe = elem(xv[k], e);
+                    const float dyv = elem(dv[k], e);
+                    float dd = fmaf(-b, xe, r * (dyv * elem(gv[j], e)));
+                    if constexpr (FUSED) dd += elem(zv[k], e);
+                    o[e] = dd;
+                    tv[j * VEC + e] = dyv * (xe * r);
+                }
+                buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(rw, off(k), make_pack<DT, VEC>(o));
+            }
+#pragma unroll
+            for (int q = 0; q < LGROUP * VEC / 4; ++q) {
+                lf32x4 v = acc_lds[k0 * VEC / 4 + q][t];
+                v += lf32x4{tv[4 * q], tv[4 * q + 1], tv[4 * q + 2], tv[4 * q + 3]};
+                acc_lds[k0 * VEC / 4 + q][t] = v;
+            }
+        }
+    }
+    // this block's dgamma sums (from its own slots: no barrier needed)
+    const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * G;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int c = t + k * LB;
+        if (c >= nchunk) continue;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int i = k * VEC + e;
+            emit_long<DT>(a, 0, c * VEC + e, acc_lds[i / 4][t][i % 4], G, pstride);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, long rows, two passes over each row (see the file comment):
+// LayerNorm, and RMSNorm on single elements (16-byte chunks do not fit the
+// row or the pointers). dgamma accumulators in LDS; LayerNorm's dbeta
+// accumulators in registers.
+// ---------------------------------------------------------------------------
+template <int DT, int VEC, int OP>
+__global__ __launch_bounds__(LB) void bwd_long_2pass_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
     constexpr int K = 64 / VEC;
     constexpr bool FUSED = OP == OPL_FUSED, LN = OP == OPL_LN;
-    constexpr int NA = LN ? 2 : 1;
     constexpr int ES = ElemSize<DT>::value;
+    static_assert((LGROUP * VEC) % 4 == 0, "whole accumulator slots per group");
+    __shared__ lf32x4 acc_lds[NSLOT][LB];
     __shared__ float slots[2 * 2 * LWAVES];
     const int N = a.N;
     const int64_t M = a.M;
     const int G = gridDim.x;
+    const int t = threadIdx.x;
     const uint32_t row_bytes = (uint32_t)N * ES;
     const int nchunk = N / VEC;
     const float inv_n = 1.0f / (float)N;
-    uint32_t coff[K];
+    auto off = [&](int k) -> uint32_t {
+        const int c = t + k * LB;
+        return c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
+    };
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int c = threadIdx.x + k * LB;
-        coff[k] = c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
-    }
+    for (int q = 0; q < NSLOT; ++q) acc_lds[q][t] = lf32x4{0.f, 0.f, 0.f, 0.f};
+    float accb[LN ? K : 1][LN ? VEC : 1];  // dbeta, LayerNorm
+#pragma unroll
+    for (int k = 0; k < (LN ? K : 1); ++k)
+#pragma unroll
+        for (int e = 0; e < (LN ? VEC : 1); ++e) accb[k][e] = 0.f;
     const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
-    float acc[NA][K][VEC];
-#pragma unroll
-    for (int q = 0; q < NA; ++q)
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[q][k][e] = 0.f;
     int parity = 0;
     for (int64_t row = blockIdx.x; row < M; row += G) {
         const rsrc_t rx = window_rsrc<ES>(a.x, row, a.ldx, 1, row_bytes);
         const rsrc_t rd = window_rsrc<ES>(a.dy, row, a.lddy, 1, row_bytes);
         const float r = buf_load_f32(make_rsrc(at(a.rstd, row, 4), 4u), 0u);
-        const float mu = LN ? buf_load_f32(make_rsrc(at(a.mean, row, 4), 4u), 0u) : 0.f;
+        float mu = 0.f;
+        if constexpr (LN) mu = buf_load_f32(make_rsrc(at(a.mean, row, 4), 4u), 0u);
         // pass 1: the row sums
         float s[2] = {0.f, 0.f};
 #pragma unroll
@@ -221,9 +354,9 @@ __global__ __launch_bounds__(LB) void bwd_long_kernel(BwdArgs a) {
             P xv[LGROUP], dv[LGROUP], gv[LGROUP];
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
-                xv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, coff[k0 + j]);
-                dv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, coff[k0 + j]);
-                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k0 + j]);
+                xv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, off(k0 + j));
+                dv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, off(k0 + j));
+                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
             }
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j)
@@ -233,6 +366,9 @@ __global__ __launch_bounds__(LB) void bwd_long_kernel(BwdArgs a) {
                     s[0] = fmaf(elem(xv[j], e) - mu, wd, s[0]);
                     if constexpr (LN) s[1] += wd;
                 }
+            // single elements: one group's loads in flight at a time, or the
+            // unrolled pass hoists all 64 chunks' loads and spills
+            if constexpr (VEC == 1) asm volatile("" ::: "memory");
         }
         float b, d = 0.f;
         if constexpr (LN) {
@@ -240,9 +376,9 @@ __global__ __launch_bounds__(LB) void bwd_long_kernel(BwdArgs a) {
             b = r * r * (s[0] * r * inv_n);  // r^2 c1, c1 = r sum (x - mu) wdy / N
             d = r * (s[1] * inv_n);          // r c2, c2 = sum wdy / N
         } else {
-            float t[1] = {s[0]};
-            block_sum<1>(t, slots, parity);
-            b = r * r * (t[0] * r * inv_n);
+            float t1[1] = {s[0]};
+            block_sum<1>(t1, slots, parity);
+            b = r * r * (t1[0] * r * inv_n);
         }
         // pass 2: dx, and the weight-gradient terms
         const rsrc_t rz = window_rsrc<ES>(a.dres, row, a.lddres, FUSED ? 1u : 0u, row_bytes);
@@ -252,11 +388,12 @@ __global__ __launch_bounds__(LB) void bwd_long_kernel(BwdArgs a) {
             P xv[LGROUP], dv[LGROUP], gv[LGROUP], zv[FUSED ? LGROUP : 1];
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
-                xv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rx, coff[k0 + j]);
-                dv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rd, coff[k0 + j]);
-                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, coff[k0 + j]);
-                if constexpr (FUSED) zv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, coff[k0 + j]);
+                xv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rx, off(k0 + j));
+                dv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rd, off(k0 + j));
+                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+                if constexpr (FUSED) zv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, off(k0 + j));
             }
+            float tv[LGROUP * VEC];
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
                 float o[VEC];
@@ -268,44 +405,32 @@ __global__ __launch_bounds__(LB) void bwd_long_kernel(BwdArgs a) {
                     if constexpr (LN) dd -= d;
                     if constexpr (FUSED) dd += elem(zv[j], e);
                     o[e] = dd;
-                    acc[0][k0 + j][e] = fmaf(dyv, xc * r, acc[0][k0 + j][e]);
-                    if constexpr (LN) acc[NA - 1][k0 + j][e] += dyv;
+                    tv[j * VEC + e] = dyv * (xc * r);
+                    if constexpr (LN) accb[k0 + j][e] += dyv;
                 }
-                buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(rw, coff[k0 + j],
+                buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(rw, off(k0 + j),
                                                                                make_pack<DT, VEC>(o));
             }
+#pragma unroll
+            for (int q = 0; q < LGROUP * VEC / 4; ++q) {
+                lf32x4 v = acc_lds[k0 * VEC / 4 + q][t];
+                v += lf32x4{tv[4 * q], tv[4 * q + 1], tv[4 * q + 2], tv[4 * q + 3]};
+                acc_lds[k0 * VEC / 4 + q][t] = v;
+            }
+            if constexpr (VEC == 1) asm volatile("" ::: "memory");
         }
     }
-
-    // this block's weight-gradient sums: a partial (two-stage sum), fp32
-    // atomics, or, with one block, the gradients themselves
+    // this block's weight-gradient sums
     const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * G;
 #pragma unroll
-    for (int q = 0; q < NA; ++q) {
-        float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
-        void *outT = q ? a.dbeta : a.dgamma;
+    for (int k = 0; k < K; ++k) {
+        const int c = t + k * LB;
+        if (c >= nchunk) continue;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int c = threadIdx.x + k * LB;
-            if (c >= nchunk) continue;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const int j = c * VEC + e;
-                const float v = acc[q][k][e];
-                if (a.mode == DG_PARTIAL) {
-                    a.partials[q * pstride + partial_index(j, blockIdx.x, G)] = v;
-                } else if (a.mode == DG_ATOMIC) {
-                    unsafeAtomicAdd(out32 + j, v);
-                } else {
-                    out32[j] = v;
-                    if (outT) {
-                        if constexpr (DT == DT_F32)
-                            static_cast<float *>(outT)[j] = v;
-                        else
-                            static_cast<uint16_t *>(outT)[j] = pack1<DT>(v);
-                    }
-                }
-            }
+        for (int e = 0; e < VEC; ++e) {
+            const int i = k * VEC + e;
+            emit_long<DT>(a, 0, c * VEC + e, acc_lds[i / 4][t][i % 4], G, pstride);
+            if constexpr (LN) emit_long<DT>(a, 1, c * VEC + e, accb[k][e], G, pstride);
         }
     }
 }
@@ -324,11 +449,16 @@ hipError_t fwd_long_vec(const FwdArgs &a, int grid, hipStream_t s) {
 template <int DT, int VEC>
 hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
     if (a.layer)
-        hipLaunchKernelGGL((bwd_long_kernel<DT, VEC, OPL_LN>), dim3(grid), dim3(LB), 0, s, a);
-    else if (a.dres)
-        hipLaunchKernelGGL((bwd_long_kernel<DT, VEC, OPL_FUSED>), dim3(grid), dim3(LB), 0, s, a);
+        hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, VEC, OPL_LN>), dim3(grid), dim3(LB), 0, s, a);
+    else if constexpr (VEC == 1) {
+        if (a.dres)
+            hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, 1, OPL_FUSED>), dim3(grid), dim3(LB), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, 1, OPL_RMS>), dim3(grid), dim3(LB), 0, s, a);
+    } else if (a.dres)
+        hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OPL_FUSED>), dim3(grid), dim3(LB), 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_long_kernel<DT, VEC, OPL_RMS>), dim3(grid), dim3(LB), 0, s, a);
+        hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OPL_RMS>), dim3(grid), dim3(LB), 0, s, a);
     return hipGetLastError();
 }
 
