@@ -538,31 +538,40 @@ def host_threads(cap=16):
 
 def cpu_baseline(w, d, budget_s=8.0, max_calls=200):
     """The CPU oracle (fp64 C, single-threaded code, unchanged) on the same
-    workload, timed two ways: one thread running whole calls, and all host
-    threads (up to 16) each running the oracle on its own contiguous shard
-    of rows, the shards' fp64 weight gradients summed afterwards (the
-    oracle call releases the interpreter lock, so the shards run in
-    parallel). Each way repeats whole calls for about `budget_s` seconds and
-    reports the median per call; `value` is the all-threads figure."""
+    workload, timed two ways: one thread running whole calls, and the host
+    threads (up to 16, never more than the rows) each running the oracle on
+    its own contiguous shard of rows, the shards' fp64 weight gradients
+    summed afterwards (the oracle call releases the interpreter lock, so the
+    shards run in parallel). Each way repeats whole calls for about
+    `budget_s` seconds and reports the median per call; `value` and `cores`
+    are the faster of the two (for a few rows, handing shards to threads
+    costs more than the work)."""
     from concurrent.futures import ThreadPoolExecutor
     call = _oracle_call(w, d)
+    abytes = algorithmic_bytes(w)
     t1, ts1 = _time_median(lambda: call(0, w.M), budget_s, max_calls)
-    nt = host_threads()
+    nt = max(1, min(host_threads(), w.M))
     bounds = [(w.M * i // nt, w.M * (i + 1) // nt) for i in range(nt)]
     with ThreadPoolExecutor(nt) as ex:
         def sharded():
             parts = list(ex.map(lambda b: call(*b), bounds))
             return [sum(p[q] for p in parts) for q in range(len(parts[0]))]
         tn, tsn = _time_median(sharded, budget_s, max_calls)
-    abytes = algorithmic_bytes(w)
-    return {"value": round(tn * 1e6, 1), "unit": "us/call", "cores": nt, "kind": "oracle",
-            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, {len(tsn)} calls "
-                      f"({sum(tsn):.1f} s) on {nt} threads, each running the fp64 C oracle on "
-                      f"1/{nt} of the rows; median per call",
-            "GBps": round(abytes / (tn * 1e6) / 1e3, 2),
-            "one_thread": {"value": round(t1 * 1e6, 1), "unit": "us/call", "cores": 1,
-                           "sample": f"{len(ts1)} whole calls ({sum(ts1):.1f} s), median",
-                           "GBps": round(abytes / (t1 * 1e6) / 1e3, 2)},
+    legs = {
+        "one_thread": {"value": round(t1 * 1e6, 1), "unit": "us/call", "cores": 1,
+                       "sample": f"{len(ts1)} whole calls ({sum(ts1):.1f} s), median",
+                       "GBps": round(abytes / (t1 * 1e6) / 1e3, 2)},
+        "all_threads": {"value": round(tn * 1e6, 1), "unit": "us/call", "cores": nt,
+                        "sample": f"{len(tsn)} calls ({sum(tsn):.1f} s), each {nt} threads running the "
+                                  f"oracle on 1/{nt} of the rows, median",
+                        "GBps": round(abytes / (tn * 1e6) / 1e3, 2)},
+    }
+    best = legs["all_threads"] if tn <= t1 else legs["one_thread"]
+    return {"value": best["value"], "unit": "us/call", "cores": best["cores"], "kind": "oracle",
+            "sample": f"the full {w.M}x{w.N} {w.dtype} workload, fp64 C oracle; the faster of one thread "
+                      f"({legs['one_thread']['value']} us) and {nt} threads on row shards "
+                      f"({legs['all_threads']['value']} us), median of whole calls",
+            "GBps": best["GBps"], **legs,
             "host": {"cpu_model": _cpu_model(), "logical_cpus": os.cpu_count()}}
 
 
@@ -590,7 +599,7 @@ def load_traffic(w):
         return None
     from hashlib import sha256
     src = b"".join(open(os.path.join(ROOT, "rmsnorm_bwd_amd", "csrc", f), "rb").read()
-                   for f in ("kernels.hip", "device.h", "plan.h", "capi.cpp"))
+                   for f in ("kernels.hip", "long_rows.hip", "device.h", "plan.h", "capi.cpp"))
     if rec.get("source_sha256") != sha256(src).hexdigest():
         return None
     return rec.get("hbm_bytes_per_call")
