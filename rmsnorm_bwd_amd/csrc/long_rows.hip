@@ -206,15 +206,19 @@ constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread
 
 // ---------------------------------------------------------------------------
 // Backward, long rows, RMSNorm on 16-byte chunks: row in registers, one
-// read; the dgamma accumulators in LDS.
+// read; the dgamma accumulators in LDS. MODE (LM_* in plan.h) says where
+// gamma lives and whether the block's next row is loaded during this one.
 // ---------------------------------------------------------------------------
-template <int DT, int VEC, int OP>
+template <int DT, int VEC, int OP, int MODE>
 __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
     constexpr int K = 64 / VEC;
     constexpr bool FUSED = OP == OPL_FUSED;
     constexpr int ES = ElemSize<DT>::value;
+    constexpr bool GRES = MODE != LM_RELOAD;  // gamma resident in registers
+    static_assert(MODE != LM_PREFETCH || ES == 2, "two rows fit beside gamma for 16-bit types only");
     static_assert((LGROUP * VEC) % 4 == 0, "whole accumulator slots per group");
+    static_assert(K % 2 == 0, "gamma fenced in pairs of chunks");
     // slot s of thread t at acc_lds[s][t]: consecutive lanes, consecutive 16 bytes
     __shared__ lf32x4 acc_lds[NSLOT][LB];
     __shared__ float slots[2 * LWAVES];
@@ -232,28 +236,58 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < NSLOT; ++q) acc_lds[q][t] = lf32x4{0.f, 0.f, 0.f, 0.f};
     const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
-    int parity = 0;
-    for (int64_t row = blockIdx.x; row < M; row += G) {
-        const rsrc_t rx = window_rsrc<ES>(a.x, row, a.ldx, 1, row_bytes);
-        const rsrc_t rd = window_rsrc<ES>(a.dy, row, a.lddy, 1, row_bytes);
-        P xv[K], dv[K], zv[FUSED ? K : 1];
+    P gres[GRES ? K : 1];
+    if constexpr (GRES) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) gres[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k));
+    }
+    auto gamma_group = [&](int k0, P (&gv)[LGROUP]) {
+#pragma unroll
+        for (int j = 0; j < LGROUP; ++j) {
+            if constexpr (GRES)
+                gv[j] = gres[k0 + j];
+            else
+                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+        }
+    };
+    // With gamma resident, an empty asm statement that "rewrites" the packed
+    // registers keeps the compiler from holding their unpacked fp32 values
+    // across the row sum or from one row to the next (that spills).
+    auto fence_gamma = [&]() {
+        if constexpr (GRES) {
+#pragma unroll
+            for (int k = 0; k < K; k += 2) opaque(gres[k], gres[k + 1]);
+        }
+    };
+    // nr = 0 (a row past the end, loaded ahead) makes every access fall
+    // outside the descriptors: no memory is touched and the values are 0.
+    auto load_row = [&](int64_t row, uint32_t nr, P (&xv)[K], P (&dv)[K]) {
+        const rsrc_t rx = window_rsrc<ES>(a.x, row, a.ldx, nr, row_bytes);
+        const rsrc_t rd = window_rsrc<ES>(a.dy, row, a.lddy, nr, row_bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             xv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rx, off(k));
             dv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rd, off(k));
         }
+    };
+    auto load_rstd = [&](int64_t row, uint32_t nr) -> float {
+        return buf_load_f32(make_rsrc(at(a.rstd, row, 4), nr * 4u), 0u);
+    };
+    auto load_dres = [&](int64_t row, P (&zv)[FUSED ? K : 1]) {
         if constexpr (FUSED) {
             const rsrc_t rz = window_rsrc<ES>(a.dres, row, a.lddres, 1, row_bytes);
 #pragma unroll
             for (int k = 0; k < K; ++k) zv[k] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rz, off(k));
         }
-        const float r = buf_load_f32(make_rsrc(at(a.rstd, row, 4), 4u), 0u);
+    };
+    int parity = 0;
+    auto process = [&](int64_t row, P (&xv)[K], P (&dv)[K], P (&zv)[FUSED ? K : 1], float r) {
+        fence_gamma();
         float s[1] = {0.f};
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += LGROUP) {
             P gv[LGROUP];
-#pragma unroll
-            for (int j = 0; j < LGROUP; ++j) gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+            gamma_group(k0, gv);
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j)
 #pragma unroll
@@ -261,13 +295,17 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
                     s[0] = fmaf(elem(xv[k0 + j], e), elem(dv[k0 + j], e) * elem(gv[j], e), s[0]);
         }
         block_sum<1>(s, slots, parity);
+        if constexpr (GRES) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
+            fence_gamma();
+        }
         const float b = r * r * (s[0] * r * inv_n);  // r^2 c1, c1 = r sum x wdy / N
         const rsrc_t rw = window_rsrc<ES>(a.dx, row, a.lddx, 1, row_bytes);
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += LGROUP) {
             P gv[LGROUP];
-#pragma unroll
-            for (int j = 0; j < LGROUP; ++j) gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+            gamma_group(k0, gv);
             float tv[LGROUP * VEC];  // this group's dy * x_hat terms
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
@@ -290,6 +328,39 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
                 v += lf32x4{tv[4 * q], tv[4 * q + 1], tv[4 * q + 2], tv[4 * q + 3]};
                 acc_lds[k0 * VEC / 4 + q][t] = v;
             }
+        }
+    };
+    if constexpr (MODE == LM_PREFETCH) {
+        // Two register sets, a and b, alternate: while one row is computed
+        // the next row of the block arrives in the other set. The next row's
+        // loads are issued after this row's dresidual_out loads and before
+        // its stores, so waiting for either never waits for the other row.
+        P xa[K], da[K], xb[K], db[K], z[FUSED ? K : 1];
+        int64_t row = blockIdx.x;  // < M: the grid has at most M blocks
+        load_row(row, 1u, xa, da);
+        float ra = load_rstd(row, 1u), rb;
+        for (;;) {
+            const uint32_t nb = row + G < M ? 1u : 0u;
+            load_dres(row, z);
+            load_row(row + G, nb, xb, db);
+            rb = load_rstd(row + G, nb);
+            process(row, xa, da, z, ra);
+            row += G;
+            if (row >= M) break;
+            const uint32_t na = row + G < M ? 1u : 0u;
+            load_dres(row, z);
+            load_row(row + G, na, xa, da);
+            ra = load_rstd(row + G, na);
+            process(row, xb, db, z, rb);
+            row += G;
+            if (row >= M) break;
+        }
+    } else {
+        for (int64_t row = blockIdx.x; row < M; row += G) {
+            P xv[K], dv[K], zv[FUSED ? K : 1];
+            load_row(row, 1u, xv, dv);
+            load_dres(row, zv);
+            process(row, xv, dv, zv, load_rstd(row, 1u));
         }
     }
     // this block's dgamma sums (from its own slots: no barrier needed)
@@ -446,6 +517,22 @@ hipError_t fwd_long_vec(const FwdArgs &a, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The RMSNorm long-row backward in the mode long_mode picks (plan.h); only
+// the modes an element size and variant can run are instantiated.
+template <int DT, int VEC, int OP>
+hipError_t bwd_long_rms(const BwdArgs &a, int grid, hipStream_t s) {
+    constexpr int ES = ElemSize<DT>::value;
+    constexpr int FAST = ES == 2 ? LM_PREFETCH : (OP == OPL_FUSED ? LM_RELOAD : LM_RESIDENT);
+    if constexpr (FAST != LM_RELOAD) {
+        if (long_mode(ES, OP == OPL_FUSED, a.M, a.N) == FAST) {
+            hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OP, FAST>), dim3(grid), dim3(LB), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OP, LM_RELOAD>), dim3(grid), dim3(LB), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int DT, int VEC>
 hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
     if (a.layer)
@@ -455,10 +542,11 @@ hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
             hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, 1, OPL_FUSED>), dim3(grid), dim3(LB), 0, s, a);
         else
             hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, 1, OPL_RMS>), dim3(grid), dim3(LB), 0, s, a);
-    } else if (a.dres)
-        hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OPL_FUSED>), dim3(grid), dim3(LB), 0, s, a);
-    else
-        hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OPL_RMS>), dim3(grid), dim3(LB), 0, s, a);
+    } else if (a.dres) {
+        return bwd_long_rms<DT, VEC, OPL_FUSED>(a, grid, s);
+    } else {
+        return bwd_long_rms<DT, VEC, OPL_RMS>(a, grid, s);
+    }
     return hipGetLastError();
 }
 

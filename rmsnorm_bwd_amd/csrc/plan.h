@@ -176,6 +176,31 @@ inline int64_t bwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool three_rea
     return steps < cap ? steps : cap;
 }
 
+// How the long-row RMSNorm backward on 16-byte chunks (long_rows.hip) runs
+// through a block's rows:
+//   LM_RELOAD    one row in flight; gamma re-read from the caches for each
+//                group of chunks.
+//   LM_RESIDENT  gamma held in registers for the whole kernel. Loads and
+//                stores retire through one in-order counter, so a gamma load
+//                issued after a group's dx stores cannot be waited on without
+//                waiting for those stores; with gamma resident nothing is
+//                waited on between a row's arrival and its last store.
+//   LM_PREFETCH  LM_RESIDENT, and the block's next row (x, dy, rstd) is
+//                loaded while the current one is computed; 16-bit types only,
+//                where two rows fit the registers beside gamma.
+// Measured on MI355X against LM_RELOAD (GPU time per call, rotated buffers,
+// 1024-8192 rows of 16400-32768 elements): fused bf16 with dresidual_out
+// 2.5-17% faster with LM_PREFETCH (fused f16 4096 x 24576: 18%); plain bf16
+// 3.6-18.7% faster up to 24576 elements and at 1024-4096 rows of 28672-32768
+// (1.7-8.1%), but slower at 8192 rows of 28672 (+1.8%) and 32768 (+8.2%);
+// plain fp32 2.8-7.8% faster with LM_RESIDENT; fused fp32 does not fit
+// gamma beside its row.
+enum : int { LM_RELOAD = 0, LM_RESIDENT = 1, LM_PREFETCH = 2 };
+inline int long_mode(int esize, bool fused, int64_t M, int64_t N) {
+    if (esize == 2) return fused || N <= 24576 || M <= 4096 ? LM_PREFETCH : LM_RELOAD;
+    return fused ? LM_RELOAD : LM_RESIDENT;
+}
+
 // dgamma combining modes actually run.
 enum : int { DG_DIRECT = 0, DG_PARTIAL = 1, DG_ATOMIC = 2 };
 

@@ -96,6 +96,16 @@ int main() {
                 if (k >= 0 && k < tiles * FIN_TILE * G) seen[k] = 1;
             }
     }
+    // the long-row backward's mode: the measured rule, and the prefetching
+    // mode only for 16-bit types (two rows fit the registers beside gamma)
+    for (int64_t M : {int64_t(1), int64_t(1024), int64_t(4096), int64_t(4097), int64_t(8192), int64_t(1) << 20})
+        for (int64_t N : {LONG_N + 1, int64_t(24576), int64_t(24577), int64_t(28672), MAX_N}) {
+            CHECK(long_mode(2, true, M, N) == LM_PREFETCH, "fused 16-bit long rows not prefetched");
+            CHECK(long_mode(2, false, M, N) == (N <= 24576 || M <= 4096 ? LM_PREFETCH : LM_RELOAD),
+                  "plain 16-bit long-row mode at M %lld N %lld", (long long)M, (long long)N);
+            CHECK(long_mode(4, false, M, N) == LM_RESIDENT, "plain fp32 long rows: gamma not resident");
+            CHECK(long_mode(4, true, M, N) == LM_RELOAD, "fused fp32 long rows: gamma does not fit");
+        }
     std::printf("plan driver: %d failed checks\n", failures);
     return failures ? 1 : 0;
 }

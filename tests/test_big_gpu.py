@@ -38,6 +38,8 @@ CASES = [  # (op, N, dtype, distinct rows)
     ("plain", 32768, "bf16", 31),    # long rows, 16-byte chunks
     ("fused", 32768, "bf16", 31),
     ("plain", 20001, "f16", 29),     # long rows, single elements
+    ("plain", 24576, "bf16", 37),    # long rows, the next row loaded during the current one
+    ("plain", 20000, "f32", 29),     # long rows, gamma held in registers
 ]
 
 

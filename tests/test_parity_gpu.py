@@ -147,7 +147,10 @@ def test_fused_short_rows_at_large_M():
 # chunks where N and the pointers allow, single elements otherwise), one row
 # per block of 512 threads; 257 rows put two rows on one block of 256.
 LONG = [(3, 16385, "bf16"), (5, 20000, "f32"), (130, 32768, "bf16"), (7, 32768, "f32"),
-        (9, 30001, "f16"), (257, 24576, "bf16"), (1, 32768, "f16"), (2, 20480, "bf16")]
+        (9, 30001, "f16"), (257, 24576, "bf16"), (1, 32768, "f16"), (2, 20480, "bf16"),
+        # several rows a block: the next row loaded during the current one
+        # (16-bit), gamma held in registers (fp32 plain)
+        (1300, 24576, "bf16"), (1100, 20000, "f32")]
 
 
 @pytest.mark.parametrize("M,N,dt", LONG)
