@@ -27,17 +27,22 @@
 // The fused forward's residual_out may be residual itself: nothing is read
 // after it is written.
 //
-// Backward, RMSNorm (plain and fused): the row (x, dy, dresidual_out) stays
-// in registers and each thread's 64 fp32 weight-gradient accumulators live
-// in LDS (128 KiB a block: a thread's own slots, so no barrier guards them),
-// so each row is read once. gamma is read with the row (it stays in the
-// caches).
+// Backward on 16-byte chunks (RMSNorm plain and fused; LayerNorm for 16-bit
+// types): the row (x, dy, dresidual_out) stays in registers and each
+// thread's 64 fp32 dgamma accumulators live in LDS (128 KiB a block: a
+// thread's own slots, so no barrier guards them), so each row is read once.
+// gamma is re-read from the caches or held in registers, and for 16-bit
+// RMSNorm the block's next row is loaded during the current one (the modes
+// of long_mode in plan.h). LayerNorm's dbeta accumulators (a second array
+// would not fit the LDS) stay in registers, which leaves room beside them
+// for a 16-bit row and gamma only.
 //
-// Backward, LayerNorm: two accumulator arrays (dgamma, dbeta) would need
-// 256 KiB of LDS, so the row is read twice instead: the first pass forms the
-// row sums (sum (x - mean)*wdy and sum wdy), the second re-reads x and dy
-// (mostly from the caches: the block read them one pass earlier), writes dx
-// and folds dy * x_hat and dy into accumulators in registers.
+// Backward in two passes (LayerNorm on fp32 rows, and every variant on
+// single elements, where N or the pointers are not 16-byte aligned): the
+// first pass forms the row sums (sum (x - mean)*wdy, and sum wdy for
+// LayerNorm), the second re-reads x and dy (mostly from the caches: the
+// block read them one pass earlier), writes dx and folds dy * x_hat (and
+// dy) into the accumulators.
 #include "device.h"
 #include "launch.h"
 #include "plan.h"
@@ -205,23 +210,24 @@ typedef float lf32x4 __attribute__((ext_vector_type(4)));
 constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread
 
 // ---------------------------------------------------------------------------
-// Backward, long rows, RMSNorm on 16-byte chunks: row in registers, one
-// read; the dgamma accumulators in LDS. MODE (LM_* in plan.h) says where
-// gamma lives and whether the block's next row is loaded during this one.
+// Backward, long rows, on 16-byte chunks, one read of each row: the row in
+// registers, the dgamma accumulators in LDS (LayerNorm's dbeta accumulators
+// in registers). MODE (LM_* in plan.h) says where gamma lives and whether
+// the block's next row is loaded during this one.
 // ---------------------------------------------------------------------------
 template <int DT, int VEC, int OP, int MODE>
-__global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
+__global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
     constexpr int K = 64 / VEC;
-    constexpr bool FUSED = OP == OPL_FUSED;
+    constexpr bool FUSED = OP == OPL_FUSED, LN = OP == OPL_LN;
     constexpr int ES = ElemSize<DT>::value;
     constexpr bool GRES = MODE != LM_RELOAD;  // gamma resident in registers
-    static_assert(MODE != LM_PREFETCH || ES == 2, "two rows fit beside gamma for 16-bit types only");
+    static_assert(MODE != LM_PREFETCH || (ES == 2 && !LN), "two rows fit beside gamma for 16-bit RMSNorm only");
     static_assert((LGROUP * VEC) % 4 == 0, "whole accumulator slots per group");
     static_assert(K % 2 == 0, "gamma fenced in pairs of chunks");
     // slot s of thread t at acc_lds[s][t]: consecutive lanes, consecutive 16 bytes
     __shared__ lf32x4 acc_lds[NSLOT][LB];
-    __shared__ float slots[2 * LWAVES];
+    __shared__ float slots[2 * (LN ? 2 : 1) * LWAVES];
     const int N = a.N;
     const int64_t M = a.M;
     const int G = gridDim.x;
@@ -235,6 +241,11 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
     };
 #pragma unroll
     for (int q = 0; q < NSLOT; ++q) acc_lds[q][t] = lf32x4{0.f, 0.f, 0.f, 0.f};
+    float accb[LN ? K : 1][LN ? VEC : 1];  // dbeta, LayerNorm
+#pragma unroll
+    for (int k = 0; k < (LN ? K : 1); ++k)
+#pragma unroll
+        for (int e = 0; e < (LN ? VEC : 1); ++e) accb[k][e] = 0.f;
     const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
     P gres[GRES ? K : 1];
     if constexpr (GRES) {
@@ -273,6 +284,10 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
     auto load_rstd = [&](int64_t row, uint32_t nr) -> float {
         return buf_load_f32(make_rsrc(at(a.rstd, row, 4), nr * 4u), 0u);
     };
+    auto load_mean = [&](int64_t row) -> float {
+        if constexpr (LN) return buf_load_f32(make_rsrc(at(a.mean, row, 4), 4u), 0u);
+        return 0.f;
+    };
     auto load_dres = [&](int64_t row, P (&zv)[FUSED ? K : 1]) {
         if constexpr (FUSED) {
             const rsrc_t rz = window_rsrc<ES>(a.dres, row, a.lddres, 1, row_bytes);
@@ -281,9 +296,12 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
         }
     };
     int parity = 0;
-    auto process = [&](int64_t row, P (&xv)[K], P (&dv)[K], P (&zv)[FUSED ? K : 1], float r) {
+    // RMSNorm: c1 = r sum x wdy / N, dx = r wdy - r^2 c1 x. LayerNorm, with
+    // xc = x - mean: c1 = r sum xc wdy / N, c2 = sum wdy / N, dx = r wdy -
+    // r^2 c1 xc - r c2.
+    auto process = [&](int64_t row, P (&xv)[K], P (&dv)[K], P (&zv)[FUSED ? K : 1], float r, float mu) {
         fence_gamma();
-        float s[1] = {0.f};
+        float s[LN ? 2 : 1] = {};
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += LGROUP) {
             P gv[LGROUP];
@@ -291,16 +309,20 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    s[0] = fmaf(elem(xv[k0 + j], e), elem(dv[k0 + j], e) * elem(gv[j], e), s[0]);
+                for (int e = 0; e < VEC; ++e) {
+                    const float wd = elem(dv[k0 + j], e) * elem(gv[j], e);
+                    s[0] = fmaf(elem(xv[k0 + j], e) - mu, wd, s[0]);
+                    if constexpr (LN) s[1] += wd;
+                }
         }
-        block_sum<1>(s, slots, parity);
+        block_sum<LN ? 2 : 1>(s, slots, parity);
         if constexpr (GRES) {
 #pragma unroll
             for (int k = 0; k < K; ++k) opaque(xv[k], dv[k]);
             fence_gamma();
         }
-        const float b = r * r * (s[0] * r * inv_n);  // r^2 c1, c1 = r sum x wdy / N
+        const float b = r * r * (s[0] * r * inv_n);  // r^2 c1
+        const float d = LN ? r * (s[LN ? 1 : 0] * inv_n) : 0.f;  // r c2
         const rsrc_t rw = window_rsrc<ES>(a.dx, row, a.lddx, 1, row_bytes);
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += LGROUP) {
@@ -313,12 +335,14 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
                 float o[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float xe = elem(xv[k], e);
+                    const float xe = elem(xv[k], e) - mu;
                     const float dyv = elem(dv[k], e);
                     float dd = fmaf(-b, xe, r * (dyv * elem(gv[j], e)));
+                    if constexpr (LN) dd -= d;
                     if constexpr (FUSED) dd += elem(zv[k], e);
                     o[e] = dd;
                     tv[j * VEC + e] = dyv * (xe * r);
+                    if constexpr (LN) accb[k][e] += dyv;
                 }
                 buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(rw, off(k), make_pack<DT, VEC>(o));
             }
@@ -344,14 +368,14 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
             load_dres(row, z);
             load_row(row + G, nb, xb, db);
             rb = load_rstd(row + G, nb);
-            process(row, xa, da, z, ra);
+            process(row, xa, da, z, ra, 0.f);
             row += G;
             if (row >= M) break;
             const uint32_t na = row + G < M ? 1u : 0u;
             load_dres(row, z);
             load_row(row + G, na, xa, da);
             ra = load_rstd(row + G, na);
-            process(row, xb, db, z, rb);
+            process(row, xb, db, z, rb, 0.f);
             row += G;
             if (row >= M) break;
         }
@@ -360,10 +384,12 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
             P xv[K], dv[K], zv[FUSED ? K : 1];
             load_row(row, 1u, xv, dv);
             load_dres(row, zv);
-            process(row, xv, dv, zv, load_rstd(row, 1u));
+            const float r = load_rstd(row, 1u);
+            process(row, xv, dv, zv, r, load_mean(row));
         }
     }
-    // this block's dgamma sums (from its own slots: no barrier needed)
+    // this block's weight-gradient sums (dgamma from its own LDS slots: no
+    // barrier needed)
     const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * G;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -373,6 +399,7 @@ __global__ __launch_bounds__(LB) void bwd_long_rms_kernel(BwdArgs a) {
         for (int e = 0; e < VEC; ++e) {
             const int i = k * VEC + e;
             emit_long<DT>(a, 0, c * VEC + e, acc_lds[i / 4][t][i % 4], G, pstride);
+            if constexpr (LN) emit_long<DT>(a, 1, c * VEC + e, accb[k][e], G, pstride);
         }
     }
 }
@@ -517,27 +544,35 @@ hipError_t fwd_long_vec(const FwdArgs &a, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The RMSNorm long-row backward in the mode long_mode picks (plan.h); only
-// the modes an element size and variant can run are instantiated.
+// The RMSNorm long-row backward on 16-byte chunks in the mode long_mode
+// picks (plan.h); only the modes an element size and variant can run are
+// instantiated.
 template <int DT, int VEC, int OP>
 hipError_t bwd_long_rms(const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int ES = ElemSize<DT>::value;
     constexpr int FAST = ES == 2 ? LM_PREFETCH : (OP == OPL_FUSED ? LM_RELOAD : LM_RESIDENT);
     if constexpr (FAST != LM_RELOAD) {
         if (long_mode(ES, OP == OPL_FUSED, a.M, a.N) == FAST) {
-            hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OP, FAST>), dim3(grid), dim3(LB), 0, s, a);
+            hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, OP, FAST>), dim3(grid), dim3(LB), 0, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((bwd_long_rms_kernel<DT, VEC, OP, LM_RELOAD>), dim3(grid), dim3(LB), 0, s, a);
+    hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, OP, LM_RELOAD>), dim3(grid), dim3(LB), 0, s, a);
     return hipGetLastError();
 }
 
 template <int DT, int VEC>
 hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
-    if (a.layer)
-        hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, VEC, OPL_LN>), dim3(grid), dim3(LB), 0, s, a);
-    else if constexpr (VEC == 1) {
+    if (a.layer) {
+        // 16-bit rows on 16-byte chunks fit the registers beside the dbeta
+        // accumulators and gamma: one read of each row; fp32 rows and single
+        // elements take two passes
+        if constexpr (ElemSize<DT>::value == 2 && VEC > 1)
+            hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, OPL_LN, LM_RESIDENT>), dim3(grid), dim3(LB), 0, s,
+                               a);
+        else
+            hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, VEC, OPL_LN>), dim3(grid), dim3(LB), 0, s, a);
+    } else if constexpr (VEC == 1) {
         if (a.dres)
             hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, 1, OPL_FUSED>), dim3(grid), dim3(LB), 0, s, a);
         else

@@ -40,6 +40,7 @@ CASES = [  # (op, N, dtype, distinct rows)
     ("plain", 20001, "f16", 29),     # long rows, single elements
     ("plain", 24576, "bf16", 37),    # long rows, the next row loaded during the current one
     ("plain", 20000, "f32", 29),     # long rows, gamma held in registers
+    ("layernorm", 24576, "bf16", 37),  # long rows, one read
 ]
 
 

@@ -132,7 +132,9 @@ def test_layernorm_atomic_mode_within_tolerance():
     check(run_case(1024, 4096, "bf16", 1e-6, flags=R.DGAMMA_ATOMIC))
 
 
-@pytest.mark.parametrize("M,N,dt", [(5, 20000, "bf16"), (3, 32768, "f32"), (260, 16400, "f16"), (4, 30003, "bf16")])
+# (1100, 24576): several rows a block through the one-read kernel
+@pytest.mark.parametrize("M,N,dt", [(5, 20000, "bf16"), (3, 32768, "f32"), (260, 16400, "f16"), (4, 30003, "bf16"),
+                                    (1100, 24576, "bf16")])
 def test_layernorm_long_rows(M, N, dt):
     print("case layernorm long rows", M, N, dt, flush=True)
     check(run_case(M, N, dt, 1e-5))
