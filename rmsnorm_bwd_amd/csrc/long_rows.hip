@@ -99,6 +99,24 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
     const rsrc_t rg = make_rsrc(a.gamma, row_bytes);
     const rsrc_t rb = make_rsrc(a.beta, LN && a.beta ? row_bytes : 0u);
     const float inv_n = 1.0f / (float)N;
+    // On 16-byte chunks gamma (and beta) stay in registers for the whole
+    // kernel, and the fused variant loads its residual row at once: no load
+    // is then issued after a row's first stores, so nothing waits on a store
+    // (loads and stores retire through one in-order counter). Measured on
+    // MI355X against loading gamma per group of chunks, two runs on two
+    // boxes: plain 8192 x 20000 bf16 -5.1 / -4.8%, plain fp32 4096 x 24576
+    // -5.7 / -2.5%, fused 4096 x 32768 bf16 -3.2 / +1.4%, LayerNorm 8192 x
+    // 20000 bf16 -0.6 / +0.5%. Single elements (64 registers of gamma a
+    // thread) keep the per-group loads.
+    constexpr bool GRES = VEC > 1;
+    P gres[GRES ? K : 1], bres[GRES && LN ? K : 1];
+    if constexpr (GRES) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            gres[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k));
+            if constexpr (LN) bres[k] = buf_load<DT, VEC, AUX_DEFAULT>(rb, off(k));
+        }
+    }
     int parity = 0;
     for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
         const rsrc_t rx = window_rsrc<ES>(a.x, row, a.ldx, 1, row_bytes);
@@ -108,13 +126,14 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
         if constexpr (FUSED) {
             const rsrc_t rr = window_rsrc<ES>(a.residual, row, a.ldres, 1, row_bytes);
             const rsrc_t ro = window_rsrc<ES>(a.residual_out, row, a.ldres_out, 1, row_bytes);
+            constexpr int RG = GRES ? K : LGROUP;  // residual chunks loaded together
 #pragma unroll
-            for (int k0 = 0; k0 < K; k0 += LGROUP) {
-                P rv[LGROUP];
+            for (int k0 = 0; k0 < K; k0 += RG) {
+                P rv[RG];
 #pragma unroll
-                for (int j = 0; j < LGROUP; ++j) rv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rr, off(k0 + j));
+                for (int j = 0; j < RG; ++j) rv[j] = buf_load<DT, VEC, AUX_STREAM_LOAD>(rr, off(k0 + j));
 #pragma unroll
-                for (int j = 0; j < LGROUP; ++j) {
+                for (int j = 0; j < RG; ++j) {
                     float t[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) t[e] = elem(av[k0 + j], e) + elem(rv[j], e);
@@ -164,8 +183,13 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
             P gv[LGROUP], bv[LN ? LGROUP : 1];
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
-                gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
-                if constexpr (LN) bv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rb, off(k0 + j));
+                if constexpr (GRES) {
+                    gv[j] = gres[k0 + j];
+                    if constexpr (LN) bv[j] = bres[LN ? k0 + j : 0];
+                } else {
+                    gv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k0 + j));
+                    if constexpr (LN) bv[j] = buf_load<DT, VEC, AUX_DEFAULT>(rb, off(k0 + j));
+                }
             }
 #pragma unroll
             for (int j = 0; j < LGROUP; ++j) {
