@@ -6,7 +6,8 @@ to the oracle too. The sample is fixed by its seed: a failure names its case
 and is reproduced by running that case again.
 
 Math: FlyDSL issue #769 ("[Feature] Add rmsnorm backward (+ forward saves
-rstd) ..."), Implementation plan: Math; FlyDSL PR #800 ("[rmsnorm] Add
+rstd) ..."), Implementation plan: Math, and PR sequence (the LayerNorm
+follow-up); FlyDSL PR #800 ("[rmsnorm] Add
 fused-add / residual backward (PR 2/3, #769)"), fused-add commit.
 """
 import numpy as np
@@ -49,6 +50,34 @@ def _cases(n=64, seed=2026):
 CASES = _cases()
 
 
+def _ln_cases(n=24, seed=2027):
+    """LayerNorm problems drawn the same way (a stream of their own, so the
+    RMSNorm sample above stays as it is); eps stays positive, since a row of
+    one element has zero variance."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(n):
+        dt = ("f32", "f16", "bf16")[int(g.integers(3))]
+        N = int(np.exp(g.uniform(0.0, np.log(32768.0))))
+        if g.random() < 0.5:
+            vw = 4 if dt == "f32" else 8
+            N = max(vw, N - N % vw)
+        N = min(max(N, 1), 32768)
+        m_max = max(1, min(3000, ELEMENTS_MAX // N))
+        M = 0 if g.random() < 0.03 else int(np.exp(g.uniform(0.0, np.log(m_max + 1.0))))
+        mode = ("auto", "auto", "deterministic", "atomic", "one_block")[int(g.integers(5))]
+        if mode == "one_block" and M * N > (1 << 17):
+            mode = "auto"
+        misalign = bool(g.random() < 0.2)
+        with_beta = bool(g.random() < 0.8)
+        eps = (1e-5, 1e-6)[int(g.integers(2))]
+        out.append((i, M, N, dt, mode, misalign, with_beta, eps, int(g.integers(1 << 30))))
+    return out
+
+
+LN_CASES = _ln_cases()
+
+
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-{c[4]}-{c[5]}"
                                               f"{'-misaligned' if c[6] else ''}{'' if c[7] else '-nodres'}"
                                               for c in CASES])
@@ -63,3 +92,13 @@ def test_random_problem(case):
     # eps = 0 with an all-zero row gives an infinite rstd, which the library
     # leaves to the caller; the draws here are never all zero
     check_case(c)
+
+
+@pytest.mark.parametrize("case", LN_CASES, ids=[f"ln{c[0]}-{c[1]}x{c[2]}-{c[3]}-{c[4]}"
+                                                 f"{'-misaligned' if c[5] else ''}{'' if c[6] else '-nobeta'}"
+                                                 for c in LN_CASES])
+def test_random_layernorm(case):
+    from test_layernorm_gpu import check, run_case
+    i, M, N, dt, mode, misalign, with_beta, eps, seed = case
+    print("case random layernorm", case, flush=True)
+    check(run_case(M, N, dt, eps, flags=MODES[mode], misalign=misalign, with_beta=with_beta, seed=seed))
