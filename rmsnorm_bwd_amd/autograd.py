@@ -24,7 +24,7 @@ Pages cited, by title:
          takes the gradient of residual_out as well; the gradient of x is
          also the gradient of residual, returned as the same tensor.
 """
-import torch
+import torch  # noqa: F401 (libtorch is loaded before the extension that links against it)
 
 _ext_module = None
 

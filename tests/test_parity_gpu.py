@@ -7,7 +7,6 @@ Math: FlyDSL issue #769 ("[Feature] Add rmsnorm backward (+ forward saves
 rstd) ..."), Implementation plan: Math; FlyDSL PR #800 ("[rmsnorm] Add
 fused-add / residual backward (PR 2/3, #769)"), fused-add commit.
 """
-import numpy as np
 import pytest
 import torch
 
