@@ -9,9 +9,10 @@
 //
 // Design. The work is bound by HBM bandwidth (about 7 flops per element
 // against 6-8 bytes), so every kernel is built to move each byte once:
-//   - rows are read with 16-byte loads (global_load_dwordx4) by consecutive
-//     lanes, and each row stays in VGPRs between the reduction and the
-//     output pass, so the backward reads x and dy from HBM exactly once;
+//   - rows are read with 16-byte loads (buffer_load_dwordx4 through buffer
+//     descriptors) by consecutive lanes, and each row stays in VGPRs between
+//     the reduction and the output pass, so the backward reads x and dy from
+//     HBM exactly once;
 //   - the next row's loads are issued before the current row is reduced, so
 //     HBM requests stay in flight across the cross-lane sum;
 //   - per-row sums use DPP and ds_swizzle inside a wavefront; rows wider than
