@@ -250,9 +250,9 @@ int layernorm_bwd_strided(const void *x, int64_t ldx, const void *gamma, const v
  * same M, N, dtype and flags) exceeds RMSN_NO_ALLOC_SCRATCH_BYTES returns
  * RMSN_ERR_SCRATCH before anything is enqueued; only rows of more than 8192
  * elements in the default and deterministic modes can need that much (the
- * atomic mode and one-workgroup calls need only the header). Other arguments, results and errors are those of
- * rmsnorm_bwd, and for the same arguments the results are bit for bit
- * those of rmsnorm_bwd. */
+ * atomic mode and one-workgroup calls need only the header). Other
+ * arguments, results and errors are those of rmsnorm_bwd, and for the same
+ * arguments the results are bit for bit those of rmsnorm_bwd. */
 int rmsnorm_bwd_no_alloc(const void *x, const void *gamma, const void *dy, const float *rstd,
                          void *dx, float *dgamma_f32, void *dgamma, int64_t M, int64_t N, int dtype,
                          unsigned flags, void *stream);
