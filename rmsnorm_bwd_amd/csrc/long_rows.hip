@@ -231,7 +231,7 @@ __device__ __forceinline__ void emit_long(const BwdArgs &a, int q, int j, float 
 }
 
 typedef float lf32x4 __attribute__((ext_vector_type(4)));
-constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread
+constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread (64 elements)
 
 // ---------------------------------------------------------------------------
 // Backward, long rows, on 16-byte chunks, one read of each row: the row in
@@ -239,18 +239,19 @@ constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread
 // in registers). MODE (LM_* in plan.h) says where gamma lives and whether
 // the block's next row is loaded during this one.
 // ---------------------------------------------------------------------------
-template <int DT, int VEC, int OP, int MODE>
+template <int DT, int VEC, int K, int OP, int MODE>
 __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
     using P = Pack<DT, VEC>;
-    constexpr int K = 64 / VEC;
+    constexpr int LG = K % LGROUP == 0 ? LGROUP : 2;  // chunks handled together
+    constexpr int NSL = K * VEC / 4;                  // float4 dgamma accumulator slots a thread
     constexpr bool FUSED = OP == OPL_FUSED, LN = OP == OPL_LN;
     constexpr int ES = ElemSize<DT>::value;
     constexpr bool GRES = MODE != LM_RELOAD;  // gamma resident in registers
     static_assert(MODE != LM_PREFETCH || (ES == 2 && !LN), "two rows fit beside gamma for 16-bit RMSNorm only");
-    static_assert((LGROUP * VEC) % 4 == 0, "whole accumulator slots per group");
+    static_assert((LG * VEC) % 4 == 0 && K % LG == 0, "whole accumulator slots per group");
     static_assert(K % 2 == 0, "gamma fenced in pairs of chunks");
     // slot s of thread t at acc_lds[s][t]: consecutive lanes, consecutive 16 bytes
-    __shared__ lf32x4 acc_lds[NSLOT][LB];
+    __shared__ lf32x4 acc_lds[NSL][LB];
     __shared__ float slots[2 * (LN ? 2 : 1) * LWAVES];
     const int N = a.N;
     const int64_t M = a.M;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
         return c < nchunk ? (uint32_t)c * (VEC * ES) : OOB;
     };
 #pragma unroll
-    for (int q = 0; q < NSLOT; ++q) acc_lds[q][t] = lf32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NSL; ++q) acc_lds[q][t] = lf32x4{0.f, 0.f, 0.f, 0.f};
     float accb[LN ? K : 1][LN ? VEC : 1];  // dbeta, LayerNorm
 #pragma unroll
     for (int k = 0; k < (LN ? K : 1); ++k)
@@ -276,9 +277,9 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) gres[k] = buf_load<DT, VEC, AUX_DEFAULT>(rg, off(k));
     }
-    auto gamma_group = [&](int k0, P (&gv)[LGROUP]) {
+    auto gamma_group = [&](int k0, P (&gv)[LG]) {
 #pragma unroll
-        for (int j = 0; j < LGROUP; ++j) {
+        for (int j = 0; j < LG; ++j) {
             if constexpr (GRES)
                 gv[j] = gres[k0 + j];
             else
@@ -327,11 +328,11 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
         fence_gamma();
         float s[LN ? 2 : 1] = {};
 #pragma unroll
-        for (int k0 = 0; k0 < K; k0 += LGROUP) {
-            P gv[LGROUP];
+        for (int k0 = 0; k0 < K; k0 += LG) {
+            P gv[LG];
             gamma_group(k0, gv);
 #pragma unroll
-            for (int j = 0; j < LGROUP; ++j)
+            for (int j = 0; j < LG; ++j)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     const float wd = elem(dv[k0 + j], e) * elem(gv[j], e);
@@ -349,12 +350,12 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
         const float d = LN ? r * (s[LN ? 1 : 0] * inv_n) : 0.f;  // r c2
         const rsrc_t rw = window_rsrc<ES>(a.dx, row, a.lddx, 1, row_bytes);
 #pragma unroll
-        for (int k0 = 0; k0 < K; k0 += LGROUP) {
-            P gv[LGROUP];
+        for (int k0 = 0; k0 < K; k0 += LG) {
+            P gv[LG];
             gamma_group(k0, gv);
-            float tv[LGROUP * VEC];  // this group's dy * x_hat terms
+            float tv[LG * VEC];  // this group's dy * x_hat terms
 #pragma unroll
-            for (int j = 0; j < LGROUP; ++j) {
+            for (int j = 0; j < LG; ++j) {
                 const int k = k0 + j;
                 float o[VEC];
 #pragma unroll
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
                 buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(rw, off(k), make_pack<DT, VEC>(o));
             }
 #pragma unroll
-            for (int q = 0; q < LGROUP * VEC / 4; ++q) {
+            for (int q = 0; q < LG * VEC / 4; ++q) {
                 lf32x4 v = acc_lds[k0 * VEC / 4 + q][t];
                 v += lf32x4{tv[4 * q], tv[4 * q + 1], tv[4 * q + 2], tv[4 * q + 3]};
                 acc_lds[k0 * VEC / 4 + q][t] = v;
@@ -571,29 +572,33 @@ hipError_t fwd_long_vec(const FwdArgs &a, int grid, hipStream_t s) {
 // The RMSNorm long-row backward on 16-byte chunks in the mode long_mode
 // picks (plan.h); only the modes an element size and variant can run are
 // instantiated.
-template <int DT, int VEC, int OP>
+template <int DT, int VEC, int K, int OP>
 hipError_t bwd_long_rms(const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int ES = ElemSize<DT>::value;
     constexpr int FAST = ES == 2 ? LM_PREFETCH : (OP == OPL_FUSED ? LM_RELOAD : LM_RESIDENT);
+    // six chunks a thread only for 16-bit rows of at most LONG6_N elements,
+    // which long_mode always runs with the next row loaded ahead
+    static_assert(K * VEC == 64 || FAST == LM_PREFETCH, "six-chunk rows are 16-bit");
     if constexpr (FAST != LM_RELOAD) {
-        if (long_mode(ES, OP == OPL_FUSED, a.M, a.N) == FAST) {
-            hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, OP, FAST>), dim3(grid), dim3(LB), 0, s, a);
+        if (K * VEC < 64 || long_mode(ES, OP == OPL_FUSED, a.M, a.N) == FAST) {
+            hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, K, OP, FAST>), dim3(grid), dim3(LB), 0, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, OP, LM_RELOAD>), dim3(grid), dim3(LB), 0, s, a);
+    if constexpr (K * VEC == 64)
+        hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, K, OP, LM_RELOAD>), dim3(grid), dim3(LB), 0, s, a);
     return hipGetLastError();
 }
 
-template <int DT, int VEC>
+template <int DT, int VEC, int K>
 hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
     if (a.layer) {
         // 16-bit rows on 16-byte chunks fit the registers beside the dbeta
         // accumulators and gamma: one read of each row; fp32 rows and single
         // elements take two passes
         if constexpr (ElemSize<DT>::value == 2 && VEC > 1)
-            hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, OPL_LN, LM_RESIDENT>), dim3(grid), dim3(LB), 0, s,
-                               a);
+            hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, VEC, K, OPL_LN, LM_RESIDENT>), dim3(grid), dim3(LB), 0,
+                               s, a);
         else
             hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, VEC, OPL_LN>), dim3(grid), dim3(LB), 0, s, a);
     } else if constexpr (VEC == 1) {
@@ -602,9 +607,9 @@ hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
         else
             hipLaunchKernelGGL((bwd_long_2pass_kernel<DT, 1, OPL_RMS>), dim3(grid), dim3(LB), 0, s, a);
     } else if (a.dres) {
-        return bwd_long_rms<DT, VEC, OPL_FUSED>(a, grid, s);
+        return bwd_long_rms<DT, VEC, K, OPL_FUSED>(a, grid, s);
     } else {
-        return bwd_long_rms<DT, VEC, OPL_RMS>(a, grid, s);
+        return bwd_long_rms<DT, VEC, K, OPL_RMS>(a, grid, s);
     }
     return hipGetLastError();
 }
@@ -612,7 +617,8 @@ hipError_t bwd_long_vec(const BwdArgs &a, int grid, hipStream_t s) {
 template <int DT>
 hipError_t fwd_long_dt(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     constexpr int VW = 16 / ElemSize<DT>::value;
-    if (p.vec == VW && p.k * VW == 64) return fwd_long_vec<DT, VW>(a, grid, s);
+    // the forward holds 64 elements a thread whatever the backward's chunk count
+    if (p.vec == VW && (p.k * VW == 64 || (VW == 8 && p.k == 6))) return fwd_long_vec<DT, VW>(a, grid, s);
     if (p.vec == 1 && p.k == 64) return fwd_long_vec<DT, 1>(a, grid, s);
     return hipErrorInvalidValue;
 }
@@ -620,8 +626,11 @@ hipError_t fwd_long_dt(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t
 template <int DT>
 hipError_t bwd_long_dt(const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int VW = 16 / ElemSize<DT>::value;
-    if (p.vec == VW && p.k * VW == 64) return bwd_long_vec<DT, VW>(a, grid, s);
-    if (p.vec == 1 && p.k == 64) return bwd_long_vec<DT, 1>(a, grid, s);
+    if (p.vec == VW && p.k * VW == 64) return bwd_long_vec<DT, VW, 64 / VW>(a, grid, s);
+    if constexpr (VW == 8) {
+        if (p.vec == 8 && p.k == 6) return bwd_long_vec<DT, 8, 6>(a, grid, s);
+    }
+    if (p.vec == 1 && p.k == 64) return bwd_long_vec<DT, 1, 64>(a, grid, s);
     return hipErrorInvalidValue;
 }
 

@@ -43,10 +43,13 @@ int main() {
                 CHECK(!vec || (vok && p.vec * esize == 16 && N % p.vec == 0), "vector plan for N = %lld", (long long)N);
                 CHECK((int64_t)p.vec * p.k * p.tpr >= N, "plan does not cover N = %lld", (long long)N);
                 CHECK(pow2(p.tpr) && p.tpr >= 16 && p.tpr <= 512, "tpr %d", p.tpr);
-                CHECK(pow2(p.k) && p.k * p.vec <= (p.long_row ? 64 : 32), "k %d vec %d at N = %lld", p.k, p.vec,
-                      (long long)N);
+                // long rows: 64 elements a thread, or six 16-byte chunks of a
+                // 16-bit row of at most LONG6_N elements
+                const bool six = p.long_row && p.vec == 8 && N <= LONG6_N;
+                CHECK(p.long_row ? p.k * p.vec == (six ? 48 : 64) : pow2(p.k) && p.k * p.vec <= 32,
+                      "k %d vec %d at N = %lld", p.k, p.vec, (long long)N);
                 CHECK(p.long_row == (N > LONG_N), "long-row plan at N = %lld", (long long)N);
-                CHECK(!p.long_row || (p.tpr == 512 && p.block == 512 && p.rpb == 1 && p.k * p.vec == 64),
+                CHECK(!p.long_row || (p.tpr == 512 && p.block == 512 && p.rpb == 1),
                       "long-row plan shape at N = %lld", (long long)N);
                 CHECK(p.block <= 512 && p.block % p.tpr == 0 && p.rpb == p.block / p.tpr, "block %d", p.block);
                 CHECK(p.block % 64 == 0, "block %d not whole wavefronts", p.block);
