@@ -49,8 +49,10 @@ def _inputs(M, N, dtype, seed):
 def test_no_alloc_matches_rmsnorm_bwd_on_two_calls_in_a_row():
     code = {"bf16": R.BF16, "f32": R.F32, "f16": R.F16}
     # the 4096 x 4096 bf16 workload, then a smaller call that uses less of the
-    # scratch and fewer workgroups
-    for M, N, dtype, seed in ((4096, 4096, "bf16", 1), (512, 2048, "bf16", 2), (300, 3000, "f32", 3)):
+    # scratch and fewer workgroups; last, long rows whose partials fill the
+    # scratch exactly (64 workgroups of 32768 columns)
+    for M, N, dtype, seed in ((4096, 4096, "bf16", 1), (512, 2048, "bf16", 2), (300, 3000, "f32", 3),
+                              (64, 32768, "bf16", 5)):
         print("case no_alloc", M, N, dtype, flush=True)
         w, d, r = _inputs(M, N, dtype, seed)
         T = w.torch_dtype
