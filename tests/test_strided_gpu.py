@@ -65,6 +65,7 @@ BWD_CASES = [
     ("50x4096_f32_elem", 50, 4096, "f32", (1, 0, 3, 0)),            # element path (one odd stride)
     ("20x20000_bf16_long_vec", 20, 20000, "bf16", (8, 16, 0, 8)),   # long rows, 16-byte chunks
     ("9x24577_f32_long_elem", 9, 24577, "f32", (1, 2, 0, 3)),       # long rows, element path
+    ("600x24576_bf16_long_vec", 600, 24576, "bf16", (8, 24, 16, 8)),  # long rows, the next row loaded ahead
 ]
 
 
