@@ -48,7 +48,7 @@ def capture(fn):
     return g
 
 
-@pytest.mark.parametrize("M,N", [(512, 2048), (300, 4096), (1, 4096), (8, 1024)])
+@pytest.mark.parametrize("M,N", [(512, 2048), (300, 4096), (1, 4096), (8, 1024), (600, 24576), (300, 32768)])
 def test_rmsnorm_forward_and_backward_replay(M, N):
     print("case graph rmsnorm", M, N, flush=True)
     dt, eps = torch.bfloat16, 1e-6
