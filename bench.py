@@ -247,32 +247,34 @@ def mode_sweep(reps=3):
                 torch.cuda.empty_cache()
 
 
-def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 4096, 16384, 32768)):
-    """The backward and the forward of plain and fused-add RMSNorm (bf16) over
-    an (M, N) grid: GPU time per call from one HIP-graph replay of `steps`
-    calls rotating over buffer sets of > 512 MiB (as the headline is timed),
-    algorithmic GB/s and its share of 8 TB/s. One JSON line per shape."""
+def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 4096, 16384, 32768), dtype="bf16"):
+    """The backward and the forward of plain and fused-add RMSNorm over an
+    (M, N) grid in one dtype: GPU time per call from one HIP-graph replay of
+    `steps` calls rotating over buffer sets of > 512 MiB (as the headline is
+    timed), algorithmic GB/s and its share of 8 TB/s. One JSON line per
+    shape."""
     dev = torch.device("cuda:0")
+    td = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     for op in ("plain", "fused"):
         for N in ns:
             for M in ms:
-                w = workloads.custom(op, M, N, "bf16", 1e-6, dy_sigma=1e-2)
-                per = (4 if op == "fused" else 3) * M * N * 2
+                w = workloads.custom(op, M, N, dtype, 1e-6, dy_sigma=1e-2)
+                per = (4 if op == "fused" else 3) * M * N * td.itemsize
                 # a replay touches at most `steps` sets; below 512 MiB in all
                 # (short shapes) the calls find their rows in the memory-side
                 # cache, as a latency-bound call of that size would in use
                 nsets = max(2, min(steps, -(-ROTATE_BYTES // per)))
-                g = (1 + 0.1 * torch.randn(N, device=dev)).to(torch.bfloat16)
+                g = (1 + 0.1 * torch.randn(N, device=dev)).to(td)
                 sets = []
                 for _ in range(nsets):
-                    x = torch.randn(M, N, device=dev).to(torch.bfloat16)
+                    x = torch.randn(M, N, device=dev).to(td)
                     _, rstd = R.rmsnorm_fwd_rstd(x, g, w.eps)
-                    t = dict(x=x, dy=(1e-2 * torch.randn(M, N, device=dev)).to(torch.bfloat16),
-                             dres=(1e-2 * torch.randn(M, N, device=dev)).to(torch.bfloat16)
+                    t = dict(x=x, dy=(1e-2 * torch.randn(M, N, device=dev)).to(td),
+                             dres=(1e-2 * torch.randn(M, N, device=dev)).to(td)
                              if op == "fused" else None,
                              rstd=rstd, dx=torch.empty_like(x), dg32=torch.empty(N, device=dev),
                              dg=torch.empty_like(g))
-                    t["ws"] = torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(M, N, torch.bfloat16)),
+                    t["ws"] = torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(M, N, td)),
                                           dtype=torch.uint8, device=dev)
                     sets.append(t)
 
@@ -285,7 +287,7 @@ def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 40
                 us = time_graph(lambda t: call_bwd(w, g, t), sets, steps, 5) * 1e3
                 us_f = time_graph(fwd, sets, steps, 5) * 1e3
                 b, bf = algorithmic_bytes(w), fwd_bytes(w)
-                print(json.dumps({"op": op, "M": M, "N": N, "dtype": "bf16", "bwd_us": round(us, 2),
+                print(json.dumps({"op": op, "M": M, "N": N, "dtype": dtype, "bwd_us": round(us, 2),
                                   "bwd_GBps": round(b / us / 1e3, 1),
                                   "bwd_pct_of_8TBps": round(100 * b / us / 1e3 / HBM_PEAK_GBPS, 1),
                                   "fwd_us": round(us_f, 2), "fwd_GBps": round(bf / us_f / 1e3, 1)}),
@@ -616,10 +618,12 @@ def main():
     ap.add_argument("--mode-sweep", action="store_true",
                     help="time the dgamma modes on an (M, N) grid (one JSON line per shape) and exit")
     ap.add_argument("--shape-sweep", action="store_true",
-                    help="time plain and fused backward and forward (bf16) on an (M, N) grid "
+                    help="time plain and fused backward and forward on an (M, N) grid "
                          "(one JSON line per shape) and exit")
     ap.add_argument("--sweep-n", default="1024,2048,4096,8192",
                     help="row lengths of --shape-sweep (comma-separated)")
+    ap.add_argument("--sweep-dtype", default="bf16", choices=("bf16", "f16", "f32"),
+                    help="element type of --shape-sweep")
     ap.add_argument("--sweep-m", default="1,128,512,1024,4096,16384,32768",
                     help="row counts of --shape-sweep (comma-separated)")
     ap.add_argument("--api-compare", action="store_true",
@@ -651,7 +655,7 @@ def main():
         return
     if args.shape_sweep:
         shape_sweep(ns=[int(v) for v in args.sweep_n.split(",")],
-                    ms=[int(v) for v in args.sweep_m.split(",")])
+                    ms=[int(v) for v in args.sweep_m.split(",")], dtype=args.sweep_dtype)
         return
     if args.floor:
         floor(workloads.WORKLOADS[args.workload])
