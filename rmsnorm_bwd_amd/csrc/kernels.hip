@@ -901,7 +901,9 @@ static hipError_t dispatch(const RowPlan &p, const A &a, int grid, hipStream_t s
         if (p.tpr == 64 && p.k == 4) return L<DT, 1, 64, 4>::go(a, grid, s);
         if (p.tpr == 64 && p.k == 8) return L<DT, 1, 64, 8>::go(a, grid, s);
         if (p.tpr == 64 && p.k == 16) return L<DT, 1, 64, 16>::go(a, grid, s);
+        if (p.tpr == 256 && p.k == 8) return L<DT, 1, 256, 8>::go(a, grid, s);
         if (p.tpr == 256 && p.k == 16) return L<DT, 1, 256, 16>::go(a, grid, s);
+        if (p.tpr == 512 && p.k == 16) return L<DT, 1, 512, 16>::go(a, grid, s);
         if (p.tpr == 512 && p.k == 32) return L<DT, 1, 512, 32>::go(a, grid, s);
     }
     return hipErrorInvalidValue;

@@ -124,10 +124,10 @@ inline bool plan_rows(int64_t N, int esize, bool vector_ok, RowPlan *p) {
             p->k = N <= 256 ? 4 : (N <= 512 ? 8 : 16);
         } else if (N <= 4096) {
             p->tpr = 256;
-            p->k = 16;
+            p->k = N <= 2048 ? 8 : 16;
         } else {
             p->tpr = 512;
-            p->k = 32;
+            p->k = N <= 8192 ? 16 : 32;
         }
     }
     p->block = block_threads(p->tpr);

@@ -42,6 +42,8 @@ CASES = [
     ("33x16384_f32", 33, 16384, "f32", 1e-6),  # eight chunks a thread
     ("300x1001_f32", 300, 1001, "f32", 1e-5),  # element path
     ("1x4096_bf16", 1, 4096, "bf16", 1e-6),    # one block writes the gradients
+    ("150x1500_f16", 150, 1500, "f16", 1e-5),  # element path, 256 threads, 8 elements a thread
+    ("200x4097_bf16", 200, 4097, "bf16", 1e-5),  # element path, 512 threads, 16 elements a thread
 ]
 
 

@@ -116,6 +116,8 @@ EDGE = [
     # a few blocks fill their window ring (and pause in the prologue) while
     # the rest hold fewer windows: 517 or 515 windows over 256 blocks
     (517, 4096, "bf16"), (1029, 2048, "bf16"), (517, 8192, "bf16"),
+    # the element path's plans with several row windows a block
+    (70, 1500, "bf16"), (600, 6001, "f16"), (300, 12289, "bf16"),
 ]
 
 
