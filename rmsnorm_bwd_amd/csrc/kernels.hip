@@ -817,7 +817,10 @@ template <int VEC, int TPR, int K, int OP> constexpr int ring_depth() {
     return d < 1 ? 1 : (d > RMSN_DEPTH ? RMSN_DEPTH : d);
 }
 
-template <int DT, int VEC, int TPR, int K>
+// PLAIN = false and LAYER = false leave the plain and the LayerNorm backward
+// out (for a plan that only the others take); a call that would need it then
+// fails with hipErrorInvalidValue.
+template <int DT, int VEC, int TPR, int K, bool PLAIN = true, bool LAYER = true>
 static hipError_t launch_bwd_cfg(const BwdArgs &a, int grid, hipStream_t s) {
     constexpr int BLOCK = block_of<TPR>();
     constexpr int RPB = BLOCK / TPR;
@@ -831,13 +834,19 @@ static hipError_t launch_bwd_cfg(const BwdArgs &a, int grid, hipStream_t s) {
     const int na = a.layer ? 2 : 1;
     const size_t lds = (size_t)(2 * na * RPB * WPR + (RPB > 1 ? fold_slots(RPB) * na * TPR * K * VEC : 0)) *
                        sizeof(float);
-    if (a.layer)
-        hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DL, OP_LN>), dim3(grid), dim3(BLOCK), lds, s, a);
-    else if (a.dres)
+    if (a.layer) {
+        if constexpr (LAYER)
+            hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DL, OP_LN>), dim3(grid), dim3(BLOCK), lds, s,
+                               a);
+        else
+            return hipErrorInvalidValue;
+    } else if (a.dres)
         hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DF, OP_RMS_FUSED>), dim3(grid), dim3(BLOCK), lds,
                            s, a);
-    else
+    else if constexpr (PLAIN)
         hipLaunchKernelGGL((bwd_main_kernel<DT, VEC, TPR, K, BLOCK, DP, OP_RMS>), dim3(grid), dim3(BLOCK), lds, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -938,9 +947,28 @@ template <int DT, int VEC, int TPR, int K> struct FwdLaunch {
     }
 };
 
+// The fused and LayerNorm backwards hold more per chunk in their ring
+// (dresidual_out; the dbeta accumulators), so rows of four 16-byte chunks a
+// thread leave them one window in flight. For rows of at most three chunks'
+// worth (1025-1536 chunks: 8200-12288 16-bit or 4100-6144 fp32 elements)
+// the fused backward, and the 16-bit LayerNorm one, take three chunks a
+// thread instead, which leaves room for two windows; the grid, the row
+// plan's other fields and the workspace are unchanged. Measured on MI355X,
+// µs per call: fused bf16 16384 x 10240 286.9 -> 225.7, 16384 x 12288
+// 310.5 -> 271.1, 4096 x 12288 86.9 -> 74.3; fused fp32 16384 x 6144
+// 281.6 -> 263.4, 4096 x 5120 68.8 -> 59.4; LayerNorm bf16 16384 x 12288
+// 230.3 -> 211.9, 4096 x 10240 65.3 -> 54.1. LayerNorm fp32 was mixed
+// (16384 x 6144 200.5 -> 209.0, 4096 x 5120 48.6 -> 47.4) and the plain
+// backward, two windows at four chunks already, slower (bf16 16384 x 12288
+// 202.0 -> 222.5): both keep four.
 template <int DT>
 static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_bwd_long(DT, p, a, grid, s);
+    constexpr int VW = 16 / ElemSize<DT>::value;
+    constexpr bool LN3 = VW == 8;
+    if ((a.dres || (LN3 && a.layer)) && p.vec == VW && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
+        (int64_t)a.N <= (int64_t)3 * RMSN_TPR_MAX * VW)
+        return launch_bwd_cfg<DT, VW, RMSN_TPR_MAX, 3, false, LN3>(a, grid, s);
     return dispatch<BwdLaunch, DT>(p, a, grid, s);
 }
 

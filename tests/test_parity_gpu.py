@@ -264,6 +264,20 @@ def test_fused_edge_shapes(M, N, dt):
     check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M * 3 + N)))
 
 
+# The fused backward runs rows of 1025 to 1536 16-byte chunks (8200-12288
+# 16-bit or 4100-6144 fp32 elements) with three chunks a thread: both ends
+# of that range, both element sizes, ragged M, a capped grid, and the first
+# row length past it (four chunks a thread).
+THREE_CHUNK = [(300, 10240, "bf16"), (129, 12288, "f16"), (260, 8200, "bf16"), (70, 6144, "f32"),
+               (65, 4100, "f32"), (4099, 12288, "bf16"), (40, 12296, "bf16")]
+
+
+@pytest.mark.parametrize("M,N,dt", THREE_CHUNK)
+def test_fused_three_chunk_rows(M, N, dt):
+    _say("case fused three-chunk", M, N, dt)
+    check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M + 7 * N)))
+
+
 @pytest.mark.parametrize("M,N,dt", [(64, 4096, "bf16"), (7, 3000, "f32"), (40, 250, "f16")])
 def test_misaligned_pointers_take_the_element_path(M, N, dt):
     _say("case misaligned", M, N, dt)
