@@ -1,6 +1,8 @@
 // long_rows.hip - forward and backward for rows of more than 16384
 // elements (up to MAX_N), where a row no longer fits the register-resident
-// window ring of kernels.hip next to the weight-gradient accumulators.
+// window ring of kernels.hip next to the weight-gradient accumulators; also
+// the fused backward of 16-bit rows of 12296-16384 elements at 4096 rows and
+// more, where that ring holds only one window.
 //
 // Pages cited, by title:
 //   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
@@ -17,7 +19,9 @@
 //
 // One row per block of 512 threads at a time; each thread owns the chunks t,
 // t + 512, ... (K of them, VEC elements each, K * VEC = 64), so a row of up
-// to 32768 elements is covered. Persistent grid: block b takes rows b, b + G,
+// to 32768 elements is covered (fewer chunks where the plan gives fewer:
+// six for 16-bit rows of at most 24576 elements, four for the fused rows of
+// at most 16384). Persistent grid: block b takes rows b, b + G,
 // ... Row tensors go through buffer descriptors whose range is the row, so
 // chunks past the row end read as zero and are not stored.
 //
@@ -650,6 +654,15 @@ hipError_t launch_bwd_long(int dtype, const RowPlan &p, const BwdArgs &a, int gr
     case DT_F32: return bwd_long_dt<DT_F32>(p, a, grid, s);
     case DT_F16: return bwd_long_dt<DT_F16>(p, a, grid, s);
     case DT_BF16: return bwd_long_dt<DT_BF16>(p, a, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_fused_next_row(int dtype, const BwdArgs &a, int grid, hipStream_t s) {
+    if (!a.dres) return hipErrorInvalidValue;
+    switch (dtype) {
+    case DT_F16: return bwd_long_rms<DT_F16, 8, 4, OPL_FUSED>(a, grid, s);
+    case DT_BF16: return bwd_long_rms<DT_BF16, 8, 4, OPL_FUSED>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -278,6 +278,34 @@ def test_fused_three_chunk_rows(M, N, dt):
     check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M + 7 * N)))
 
 
+# From 4096 rows the fused backward runs 16-bit rows of 12296-16384 elements
+# on the long-row kernel, which loads a block's next row during the current
+# one: ragged M on the capped grid, both 16-bit types, both ends of the range
+# (2048 rows stay on the main kernel).
+FUSED_NEXT_ROW = [(4099, 12296, "bf16"), (4096, 16384, "f16"), (4100, 14336, "bf16"), (2048, 16384, "bf16")]
+
+
+@pytest.mark.parametrize("M,N,dt", FUSED_NEXT_ROW)
+def test_fused_next_row_kernel_rows(M, N, dt):
+    _say("case fused next-row", M, N, dt)
+    check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M + 11 * N)))
+
+
+def test_fused_next_row_kernel_every_dgamma_mode():
+    """The atomic and one-block sums on the same inputs: dx bit-equal to the
+    default call's (it does not depend on how dgamma is summed), dgamma
+    within the tolerance of the oracle."""
+    _say("case fused next-row, modes")
+    c = fused_case(workloads.custom("fused", 4097, 12296, "bf16", 1e-6, seed=21))
+    check_case(c)
+    ag, gg, dyg, dresg, rg = c["inputs"]
+    for flags in (R.DGAMMA_ATOMIC, R.DGAMMA_ONE_BLOCK):
+        dx, dg32, _ = R.fused_add_rmsnorm_bwd(ag, gg, dyg, dresg, rg, flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(dx, c["dx"][0]), f"flags {flags}: dx differs from the default call"
+        assert rel(dg32, c["dg32"][1]) <= tol_dgamma(c["M"]), f"flags {flags}: dgamma"
+
+
 @pytest.mark.parametrize("M,N,dt", [(64, 4096, "bf16"), (7, 3000, "f32"), (40, 250, "f16")])
 def test_misaligned_pointers_take_the_element_path(M, N, dt):
     _say("case misaligned", M, N, dt)

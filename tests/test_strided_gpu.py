@@ -89,7 +89,15 @@ def test_rmsnorm_bwd_strided(name, M, N, dt, pads):
     assert gaps_untouched(dxbuf, N), "dx wrote between rows"
 
 
-@pytest.mark.parametrize("name,M,N,dt,pads", BWD_CASES[1::2], ids=[c[0] for c in BWD_CASES[1::2]])
+# the fused backward's own row plans: three chunks a thread, and from 4096
+# rows the long-row kernel for rows of 12296-16384 16-bit elements
+FUSED_CASES = BWD_CASES[1::2] + [
+    ("300x12288_bf16_three_chunk", 300, 12288, "bf16", (8, 0, 16, 8)),
+    ("4097x12296_bf16_next_row", 4097, 12296, "bf16", (8, 16, 24, 8)),
+]
+
+
+@pytest.mark.parametrize("name,M,N,dt,pads", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
 def test_fused_bwd_strided(name, M, N, dt, pads):
     print("case strided fused bwd", name, flush=True)
     td = T[dt]
