@@ -234,8 +234,11 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
     // from 19.0 to 18.5 us and leaves 4096 x 4096 unchanged or faster, while at
     // 32 values a thread 1024 x 16384 goes from 27.4 to 36.7 us).
     constexpr bool KEEP = K * VEC <= 16;
+    //
+    // acc_on = false leaves the weight-gradient accumulators alone (the last
+    // group's terms are added beforehand by `accumulate`, below).
     auto compute = [&](P (&xv)[K], P (&dv)[K], P (&rv)[FUSED ? K : 1], float r, float mu, int &parity,
-                       P (&out)[K]) {
+                       P (&out)[K], bool acc_on) {
         float b, d = 0.f;
         float xk[KEEP ? K : 1][KEEP ? VEC : 1], wk[KEEP ? K : 1][KEEP ? VEC : 1];
         if constexpr (LN) {
@@ -298,8 +301,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
                 if constexpr (LN) dd -= d;
                 if constexpr (FUSED) dd += elem(rv[k], e);
                 o[e] = dd;
-                acc[0][k][e] = fmaf(dyv, xv_e * r2, acc[0][k][e]);
-                if constexpr (LN) acc[NA - 1][k][e] += dyv;
+                if (acc_on) {
+                    acc[0][k][e] = fmaf(dyv, xv_e * r2, acc[0][k][e]);
+                    if constexpr (LN) acc[NA - 1][k][e] += dyv;
+                }
             }
             out[k] = make_pack<DT, VEC>(o);
         }
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
         for (int s = 0; s < DEPTH; ++s) {
             const int64_t wb = base + s * wstride;
             P out[K];
-            compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out);
+            compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out, true);
             settle(out);
             load_window(wb + DEPTH * wstride, xs[s], ds[s], rs[s], rr[s], mr[s]);
             store_dx(wb, out);
@@ -367,164 +372,208 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             consume(ds[s][k]);
             if constexpr (FUSED) consume(rs[s][k]);
         }
-    // The last, partial group (block-uniform test): its rows are loaded.
-#pragma unroll
-    for (int s = 0; s < DEPTH - 1; ++s) {
-        const int64_t wb = base + s * wstride;
-        if (wb < M) {
-            P out[K];
-            compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out);
-            store_dx(wb, out);
-        }
-    }
-
     // ---- this block's weight-gradient partials (dgamma; dbeta for LayerNorm) ----
     // Partials go to the workspace in 16-byte stores where the columns allow;
     // array q of the tiled partials starts q * pstride floats in.
-    const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * gridDim.x;
-    auto emit1 = [&](int q, int j, float v) {
-        float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
-        void *outT = q ? a.dbeta : a.dgamma;
-        if (a.mode == DG_PARTIAL) {
-            partial_store(v, a.partials + q * pstride + partial_index(j, blockIdx.x, gridDim.x));
-        } else if (a.mode == DG_ATOMIC) {
-            unsafeAtomicAdd(out32 + j, v);
-        } else {
-            out32[j] = v;
-            if (outT) {
-                if constexpr (DT == DT_F32) {
-                    static_cast<float *>(outT)[j] = v;
-                } else {
-                    static_cast<uint16_t *>(outT)[j] = pack1<DT>(v);
-                }
-            }
-        }
-    };
-    // One block writing the gradients itself stores four columns at once (a
-    // 16-byte store of the fp32 sums, an 8- or 16-byte store of their dtype
-    // copy) where every output is aligned for it: scattered element stores
-    // from a single CU are what bound a one-block call (measured on MI355X,
-    // one row of 8192 bf16 columns: 8.1 us with element stores).
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    constexpr uintptr_t TA = DT == DT_F32 ? 15 : 7;  // alignment mask of a 4-column dtype copy
-    constexpr bool USES_EMIT4 = RPB > 1 || VEC % 4 == 0;  // else only element stores are made
-    const bool direct_vec =
-        USES_EMIT4 && a.mode == DG_DIRECT && ((reinterpret_cast<uintptr_t>(a.dgamma_f32) & 15) == 0) &&
-        ((reinterpret_cast<uintptr_t>(a.dgamma) & TA) == 0) &&
-        (NA == 1 || (((reinterpret_cast<uintptr_t>(a.dbeta_f32) & 15) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(a.dbeta) & TA) == 0)));
-    // four consecutive columns j..j+3 (j a multiple of 4, all < N) lie in one
-    // partial tile, so one 16-byte store writes them
-    auto emit4 = [&](int q, int j, float v0, float v1, float v2, float v3) {
-        if (a.mode == DG_PARTIAL) {
-            f32x4 v = {v0, v1, v2, v3};
-            partial_store(v, reinterpret_cast<f32x4 *>(a.partials + q * pstride +
-                                                       partial_index(j, blockIdx.x, gridDim.x)));
-        } else if (direct_vec) {
+    auto emit_partials = [&]() {
+        const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * gridDim.x;
+        auto emit1 = [&](int q, int j, float v) {
             float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
             void *outT = q ? a.dbeta : a.dgamma;
-            *reinterpret_cast<f32x4 *>(out32 + j) = f32x4{v0, v1, v2, v3};
-            if (outT) {
-                if constexpr (DT == DT_F32) {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(outT) + j) = f32x4{v0, v1, v2, v3};
-                } else {
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(outT) + j) =
-                        u32x2{pack2<DT>(v0, v1), pack2<DT>(v2, v3)};
-                }
-            }
-        } else {
-            emit1(q, j, v0);
-            emit1(q, j + 1, v1);
-            emit1(q, j + 2, v2);
-            emit1(q, j + 3, v3);
-        }
-    };
-    if constexpr (RPB == 1) {
-#pragma unroll
-        for (int q = 0; q < NA; ++q)
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int c = lt + k * TPR;
-                if (c < nchunk) {
-                    if constexpr (VEC % 4 == 0) {
-#pragma unroll
-                        for (int e = 0; e < VEC; e += 4)
-                            emit4(q, c * VEC + e, acc[q][k][e], acc[q][k][e + 1], acc[q][k][e + 2],
-                                  acc[q][k][e + 3]);
+            if (a.mode == DG_PARTIAL) {
+                partial_store(v, a.partials + q * pstride + partial_index(j, blockIdx.x, gridDim.x));
+            } else if (a.mode == DG_ATOMIC) {
+                unsafeAtomicAdd(out32 + j, v);
+            } else {
+                out32[j] = v;
+                if (outT) {
+                    if constexpr (DT == DT_F32) {
+                        static_cast<float *>(outT)[j] = v;
                     } else {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) emit1(q, c * VEC + e, acc[q][k][e]);
+                        static_cast<uint16_t *>(outT)[j] = pack1<DT>(v);
                     }
                 }
             }
-    } else {
-        // Fold the rpb row groups in a fixed order and leave the block's total
-        // in slot 0, from which all threads write it out. With 8 or more
-        // groups, pairwise: in the round of half-width h (rpb/2, rpb/4, ...,
-        // 1) groups h..2h-1 leave their sums in exchange slot g - h and groups
-        // 0..h-1 add them (group 0 ends with ((g0 + g8) + (g4 + g12)) + ...),
-        // 2 log2(rpb) barriers instead of one a group; with fewer groups, one
-        // group after another into slot 0. Measured on MI355X (GPU time per
-        // call): 16 groups, 8 x 256 fp32 7.1 -> 4.2 us, 32 x 256 bf16 6.1 ->
-        // 4.5 us, 16384 x 512 bf16 18.1 -> 14.1 us, 32768 x 256 bf16 14.3 ->
-        // 12.5 us; 4 groups are 0.1 us faster one after another.
-        constexpr int CS = TPR * K * VEC;  // floats of one array in a slot
-        auto slot_io = [&](int s, bool add) {
-            float *sl = comb + s * (NA * CS);
+        };
+        // One block writing the gradients itself stores four columns at once (a
+        // 16-byte store of the fp32 sums, an 8- or 16-byte store of their dtype
+        // copy) where every output is aligned for it: scattered element stores
+        // from a single CU are what bound a one-block call (measured on MI355X,
+        // one row of 8192 bf16 columns: 8.1 us with element stores).
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        constexpr uintptr_t TA = DT == DT_F32 ? 15 : 7;  // alignment mask of a 4-column dtype copy
+        constexpr bool USES_EMIT4 = RPB > 1 || VEC % 4 == 0;  // else only element stores are made
+        const bool direct_vec =
+            USES_EMIT4 && a.mode == DG_DIRECT && ((reinterpret_cast<uintptr_t>(a.dgamma_f32) & 15) == 0) &&
+            ((reinterpret_cast<uintptr_t>(a.dgamma) & TA) == 0) &&
+            (NA == 1 || (((reinterpret_cast<uintptr_t>(a.dbeta_f32) & 15) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(a.dbeta) & TA) == 0)));
+        // four consecutive columns j..j+3 (j a multiple of 4, all < N) lie in one
+        // partial tile, so one 16-byte store writes them
+        auto emit4 = [&](int q, int j, float v0, float v1, float v2, float v3) {
+            if (a.mode == DG_PARTIAL) {
+                f32x4 v = {v0, v1, v2, v3};
+                partial_store(v, reinterpret_cast<f32x4 *>(a.partials + q * pstride +
+                                                           partial_index(j, blockIdx.x, gridDim.x)));
+            } else if (direct_vec) {
+                float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
+                void *outT = q ? a.dbeta : a.dgamma;
+                *reinterpret_cast<f32x4 *>(out32 + j) = f32x4{v0, v1, v2, v3};
+                if (outT) {
+                    if constexpr (DT == DT_F32) {
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(outT) + j) = f32x4{v0, v1, v2, v3};
+                    } else {
+                        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(outT) + j) =
+                            u32x2{pack2<DT>(v0, v1), pack2<DT>(v2, v3)};
+                    }
+                }
+            } else {
+                emit1(q, j, v0);
+                emit1(q, j + 1, v1);
+                emit1(q, j + 2, v2);
+                emit1(q, j + 3, v3);
+            }
+        };
+        if constexpr (RPB == 1) {
 #pragma unroll
             for (int q = 0; q < NA; ++q)
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     const int c = lt + k * TPR;
-                    if (c < nchunk)
+                    if (c < nchunk) {
+                        if constexpr (VEC % 4 == 0) {
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) {
-                            float *p = sl + q * CS + c * VEC + e;
-                            if (add)
-                                acc[q][k][e] += *p;
-                            else
-                                *p = acc[q][k][e];
+                            for (int e = 0; e < VEC; e += 4)
+                                emit4(q, c * VEC + e, acc[q][k][e], acc[q][k][e + 1], acc[q][k][e + 2],
+                                      acc[q][k][e + 3]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) emit1(q, c * VEC + e, acc[q][k][e]);
                         }
+                    }
                 }
-        };
-        if constexpr (RPB >= FOLD_TREE_MIN) {
-#pragma unroll
-            for (int h = RPB / 2; h >= 1; h >>= 1) {
-                if (grp >= h && grp < 2 * h) slot_io(grp - h, false);
-                __syncthreads();
-                if (grp < h) {
-                    slot_io(grp, true);
-                    if (h == 1) slot_io(0, false);
-                }
-                __syncthreads();
-            }
         } else {
-            for (int gi = 0; gi < RPB; ++gi) {
-                if (grp == gi) {
+            // Fold the rpb row groups in a fixed order and leave the block's total
+            // in slot 0, from which all threads write it out. With 8 or more
+            // groups, pairwise: in the round of half-width h (rpb/2, rpb/4, ...,
+            // 1) groups h..2h-1 leave their sums in exchange slot g - h and groups
+            // 0..h-1 add them (group 0 ends with ((g0 + g8) + (g4 + g12)) + ...),
+            // 2 log2(rpb) barriers instead of one a group; with fewer groups, one
+            // group after another into slot 0. Measured on MI355X (GPU time per
+            // call): 16 groups, 8 x 256 fp32 7.1 -> 4.2 us, 32 x 256 bf16 6.1 ->
+            // 4.5 us, 16384 x 512 bf16 18.1 -> 14.1 us, 32768 x 256 bf16 14.3 ->
+            // 12.5 us; 4 groups are 0.1 us faster one after another.
+            constexpr int CS = TPR * K * VEC;  // floats of one array in a slot
+            auto slot_io = [&](int s, bool add) {
+                float *sl = comb + s * (NA * CS);
 #pragma unroll
-                    for (int q = 0; q < NA; ++q)
+                for (int q = 0; q < NA; ++q)
 #pragma unroll
-                        for (int k = 0; k < K; ++k) {
-                            const int c = lt + k * TPR;
-                            if (c < nchunk)
+                    for (int k = 0; k < K; ++k) {
+                        const int c = lt + k * TPR;
+                        if (c < nchunk)
 #pragma unroll
-                                for (int e = 0; e < VEC; ++e) {
-                                    float *cq = comb + q * CS + c * VEC + e;
-                                    *cq = gi == 0 ? acc[q][k][e] : *cq + acc[q][k][e];
-                                }
-                        }
+                            for (int e = 0; e < VEC; ++e) {
+                                float *p = sl + q * CS + c * VEC + e;
+                                if (add)
+                                    acc[q][k][e] += *p;
+                                else
+                                    *p = acc[q][k][e];
+                            }
+                    }
+            };
+            if constexpr (RPB >= FOLD_TREE_MIN) {
+#pragma unroll
+                for (int h = RPB / 2; h >= 1; h >>= 1) {
+                    if (grp >= h && grp < 2 * h) slot_io(grp - h, false);
+                    __syncthreads();
+                    if (grp < h) {
+                        slot_io(grp, true);
+                        if (h == 1) slot_io(0, false);
+                    }
+                    __syncthreads();
                 }
-                __syncthreads();
+            } else {
+                for (int gi = 0; gi < RPB; ++gi) {
+                    if (grp == gi) {
+#pragma unroll
+                        for (int q = 0; q < NA; ++q)
+#pragma unroll
+                            for (int k = 0; k < K; ++k) {
+                                const int c = lt + k * TPR;
+                                if (c < nchunk)
+#pragma unroll
+                                    for (int e = 0; e < VEC; ++e) {
+                                        float *cq = comb + q * CS + c * VEC + e;
+                                        *cq = gi == 0 ? acc[q][k][e] : *cq + acc[q][k][e];
+                                    }
+                            }
+                    }
+                    __syncthreads();
+                }
+            }
+            const int n4 = N & ~3;
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const float *cq = comb + q * CS;  // slot 0
+                for (int j = threadIdx.x * 4; j < n4; j += BLOCK * 4)
+                    emit4(q, j, cq[j], cq[j + 1], cq[j + 2], cq[j + 3]);
+                for (int j = n4 + threadIdx.x; j < N; j += BLOCK) emit1(q, j, cq[j]);
             }
         }
-        const int n4 = N & ~3;
+    };
+
+    // A window's weight-gradient terms, as `compute` forms them.
+    auto accumulate = [&](const P (&xv)[K], const P (&dv)[K], float r, float mu) {
 #pragma unroll
-        for (int q = 0; q < NA; ++q) {
-            const float *cq = comb + q * CS;  // slot 0
-            for (int j = threadIdx.x * 4; j < n4; j += BLOCK * 4) emit4(q, j, cq[j], cq[j + 1], cq[j + 2], cq[j + 3]);
-            for (int j = n4 + threadIdx.x; j < N; j += BLOCK) emit1(q, j, cq[j]);
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float xv_e = LN ? elem(xv[k], e) - mu : elem(xv[k], e);
+                const float dyv = elem(dv[k], e);
+                acc[0][k][e] = fmaf(dyv, xv_e * r, acc[0][k][e]);
+                if constexpr (LN) acc[NA - 1][k][e] += dyv;
+            }
+    };
+    // The last, partial group (block-uniform tests): its rows are loaded.
+    // With one row a window its weight-gradient terms, which need the saved
+    // statistics but not the row sums, are added first and the block's
+    // partials go out before the group's row sums and dx, overlapping them
+    // instead of trailing the last dx stores. The sums take the same rows in
+    // the same order either way, so the results are bit-identical. Measured
+    // on MI355X, bf16, µs per call: fused 1024 x 8192 17.9-18.0 -> 17.3-17.5,
+    // LayerNorm 4096 x 4096 23.0-23.6 -> 22.8, plain 512 x 8192 11.8 -> 11.1,
+    // 128 x 4096 6.45 -> 6.2-6.3; 4096 x 4096, 16384 x 4096 and 32768 x 8192
+    // unchanged. Blocks of several rows, whose fold across row groups takes
+    // barriers, lost 2-5% with it (128 x 1024 6.3 -> 6.5-6.6, fused 512 x
+    // 2048 7.4 -> 7.6) and store after the group, as does a block whose
+    // windows fill whole groups (it has no partial group).
+    if (RPB == 1 && base < M) {
+#pragma unroll
+        for (int s = 0; s < DEPTH - 1; ++s)
+            if (base + s * wstride < M) accumulate(xs[s], ds[s], rr[s], mr[s]);
+        emit_partials();
+#pragma unroll
+        for (int s = 0; s < DEPTH - 1; ++s) {
+            const int64_t wb = base + s * wstride;
+            if (wb < M) {
+                P out[K];
+                compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out, false);
+                store_dx(wb, out);
+            }
         }
+    } else {
+#pragma unroll
+        for (int s = 0; s < DEPTH - 1; ++s) {
+            const int64_t wb = base + s * wstride;
+            if (wb < M) {
+                P out[K];
+                compute(xs[s], ds[s], rs[s], rr[s], mr[s], parity, out, true);
+                store_dx(wb, out);
+            }
+        }
+        emit_partials();
     }
 }
 
