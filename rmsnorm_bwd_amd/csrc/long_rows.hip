@@ -237,6 +237,35 @@ __device__ __forceinline__ void emit_long(const BwdArgs &a, int q, int j, float 
 typedef float lf32x4 __attribute__((ext_vector_type(4)));
 constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread (64 elements)
 
+// A thread's sums of array q for its chunk c (VEC columns from c * VEC):
+// partials in 16-byte stores (four consecutive columns, a multiple of 4 from
+// the row start, lie in one partial tile), else one column at a time.
+template <int DT, int VEC, int K, bool LN>
+__device__ __forceinline__ void emit_chunk(const BwdArgs &a, int t, int c, int k, const lf32x4 (*acc)[LB],
+                                           const float (&accb)[LN ? K : 1][LN ? VEC : 1], int G,
+                                           int64_t pstride) {
+    if constexpr (VEC % 4 == 0) {
+        if (a.mode == DG_PARTIAL) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const int i = k * VEC + e;
+                const int64_t p = partial_index(c * VEC + e, blockIdx.x, G);
+                *reinterpret_cast<lf32x4 *>(a.partials + p) = acc[i / 4][t];
+                if constexpr (LN)
+                    *reinterpret_cast<lf32x4 *>(a.partials + pstride + p) =
+                        lf32x4{accb[k][e], accb[k][e + 1], accb[k][e + 2], accb[k][e + 3]};
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const int i = k * VEC + e;
+        emit_long<DT>(a, 0, c * VEC + e, acc[i / 4][t][i % 4], G, pstride);
+        if constexpr (LN) emit_long<DT>(a, 1, c * VEC + e, accb[k][e], G, pstride);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Backward, long rows, on 16-byte chunks, one read of each row: the row in
 // registers, the dgamma accumulators in LDS (LayerNorm's dbeta accumulators
@@ -420,16 +449,15 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
     // this block's weight-gradient sums (dgamma from its own LDS slots: no
     // barrier needed)
     const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * G;
+    // the thread index passes through an empty asm here, so that the address
+    // arithmetic of these stores is not hoisted into the row loop, where its
+    // registers would spill
+    int te = t;
+    asm volatile("" : "+v"(te));
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int c = t + k * LB;
-        if (c >= nchunk) continue;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int i = k * VEC + e;
-            emit_long<DT>(a, 0, c * VEC + e, acc_lds[i / 4][t][i % 4], G, pstride);
-            if constexpr (LN) emit_long<DT>(a, 1, c * VEC + e, accb[k][e], G, pstride);
-        }
+        const int c = te + k * LB;
+        if (c < nchunk) emit_chunk<DT, VEC, K, LN>(a, te, c, k, acc_lds, accb, G, pstride);
     }
 }
 
@@ -549,16 +577,15 @@ __global__ __launch_bounds__(LB) void bwd_long_2pass_kernel(BwdArgs a) {
     }
     // this block's weight-gradient sums
     const int64_t pstride = (int64_t)((N + FIN_TILE - 1) / FIN_TILE) * FIN_TILE * G;
+    // the thread index passes through an empty asm here, so that the address
+    // arithmetic of these stores is not hoisted into the row loop, where its
+    // registers would spill
+    int te = t;
+    asm volatile("" : "+v"(te));
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int c = t + k * LB;
-        if (c >= nchunk) continue;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int i = k * VEC + e;
-            emit_long<DT>(a, 0, c * VEC + e, acc_lds[i / 4][t][i % 4], G, pstride);
-            if constexpr (LN) emit_long<DT>(a, 1, c * VEC + e, accb[k][e], G, pstride);
-        }
+        const int c = te + k * LB;
+        if (c < nchunk) emit_chunk<DT, VEC, K, LN>(a, te, c, k, acc_lds, accb, G, pstride);
     }
 }
 
