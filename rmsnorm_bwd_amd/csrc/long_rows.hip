@@ -237,9 +237,43 @@ __device__ __forceinline__ void emit_long(const BwdArgs &a, int q, int j, float 
 typedef float lf32x4 __attribute__((ext_vector_type(4)));
 constexpr int NSLOT = 64 / 4;  // float4 dgamma accumulator slots a thread (64 elements)
 
+// Whether one block writing the gradients itself may store four columns at
+// once: the fp32 outputs 16-byte aligned, their dtype copies aligned for four
+// values (8 bytes, 16 for fp32).
+template <int DT>
+__device__ __forceinline__ bool direct_vec_ok(const BwdArgs &a, bool ln) {
+    constexpr uintptr_t TA = DT == DT_F32 ? 15 : 7;
+    const bool g = ((reinterpret_cast<uintptr_t>(a.dgamma_f32) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(a.dgamma) & TA) == 0);
+    const bool b = !ln || (((reinterpret_cast<uintptr_t>(a.dbeta_f32) & 15) == 0) &&
+                           ((reinterpret_cast<uintptr_t>(a.dbeta) & TA) == 0));
+    return g && b;
+}
+
+// Columns j..j+3 of array q (0 dgamma, 1 dbeta) written by the one block that
+// runs the call: the fp32 sums in one 16-byte store, their dtype copy in one
+// more.
+template <int DT>
+__device__ __forceinline__ void emit_direct4(const BwdArgs &a, int q, int j, lf32x4 v) {
+    typedef uint32_t lu32x2 __attribute__((ext_vector_type(2)));
+    float *out32 = q ? a.dbeta_f32 : a.dgamma_f32;
+    void *outT = q ? a.dbeta : a.dgamma;
+    *reinterpret_cast<lf32x4 *>(out32 + j) = v;
+    if (outT) {
+        if constexpr (DT == DT_F32)
+            *reinterpret_cast<lf32x4 *>(static_cast<float *>(outT) + j) = v;
+        else
+            *reinterpret_cast<lu32x2 *>(static_cast<uint16_t *>(outT) + j) =
+                lu32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+    }
+}
+
 // A thread's sums of array q for its chunk c (VEC columns from c * VEC):
 // partials in 16-byte stores (four consecutive columns, a multiple of 4 from
-// the row start, lie in one partial tile), else one column at a time.
+// the row start, lie in one partial tile), the gradients of a one-block call
+// four columns at a time where the outputs are aligned for it (a single CU
+// storing element by element is what bounds such a call), else one column
+// at a time.
 template <int DT, int VEC, int K, bool LN>
 __device__ __forceinline__ void emit_chunk(const BwdArgs &a, int t, int c, int k, const lf32x4 (*acc)[LB],
                                            const float (&accb)[LN ? K : 1][LN ? VEC : 1], int G,
@@ -254,6 +288,17 @@ __device__ __forceinline__ void emit_chunk(const BwdArgs &a, int t, int c, int k
                 if constexpr (LN)
                     *reinterpret_cast<lf32x4 *>(a.partials + pstride + p) =
                         lf32x4{accb[k][e], accb[k][e + 1], accb[k][e + 2], accb[k][e + 3]};
+            }
+            return;
+        }
+        if (a.mode == DG_DIRECT && direct_vec_ok<DT>(a, LN)) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const int i = k * VEC + e;
+                emit_direct4<DT>(a, 0, c * VEC + e, acc[i / 4][t]);
+                if constexpr (LN)
+                    emit_direct4<DT>(a, 1, c * VEC + e,
+                                     lf32x4{accb[k][e], accb[k][e + 1], accb[k][e + 2], accb[k][e + 3]});
             }
             return;
         }

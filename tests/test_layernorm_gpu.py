@@ -152,6 +152,27 @@ def test_layernorm_one_block_mode(M, N, dt):
     check(run_case(M, N, dt, 1e-5, flags=R.DGAMMA_ONE_BLOCK))
 
 
+@pytest.mark.parametrize("N,dt", [(20000, "bf16"), (24576, "f16"), (20000, "f32")])
+def test_layernorm_one_long_row_unaligned_gradient_outputs(N, dt):
+    """One long row: one block writes dgamma and dbeta itself, four columns a
+    store where the outputs allow; outputs that are only element-aligned
+    take element stores and must hold the same bits."""
+    print("case layernorm one long row, unaligned outputs", N, dt, flush=True)
+    c = run_case(1, N, dt, 1e-5)
+    check(c)
+    td = T[dt]
+    x, g, b, dy = _inputs(1, N, dt)
+    mean, rstd = c["mean"][1].to(DEV), c["rstd"][1].to(DEV)
+    bufs = [torch.empty(N + 1, dtype=t, device=DEV) for t in (torch.float32, torch.float32, td, td)]
+    _, dg32, db32, dgt, dbt = R.layernorm_bwd(x.to(DEV), g.to(DEV), dy.to(DEV), mean, rstd,
+                                              dgamma_f32=bufs[0][1:], dbeta_f32=bufs[1][1:],
+                                              dgamma=bufs[2][1:], dbeta=bufs[3][1:])
+    torch.cuda.synchronize()
+    assert bufs[0][1:].data_ptr() % 16 != 0
+    for got, ref in ((dg32, c["dg"][0]), (db32, c["db"][0]), (dgt, c["dgt"]), (dbt, c["dbt"])):
+        assert torch.equal(got.cpu(), ref.cpu())
+
+
 def test_layernorm_no_rows_gives_zero_gradients():
     N = 512
     g = torch.ones(N, dtype=torch.bfloat16, device=DEV)

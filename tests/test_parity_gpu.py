@@ -314,7 +314,9 @@ def test_misaligned_pointers_take_the_element_path(M, N, dt):
 
 
 @pytest.mark.parametrize("M,N,dt", [(1, 4096, "bf16"), (8, 1024, "bf16"), (32, 256, "bf16"),
-                                     (1, 3000, "f32"), (8, 256, "f16")])
+                                     (1, 3000, "f32"), (8, 256, "f16"),
+                                     # one long row: the long-row kernels' one-block stores
+                                     (1, 20000, "bf16"), (1, 32768, "f32"), (1, 24576, "f16")])
 def test_one_block_call_with_unaligned_gradient_outputs(M, N, dt):
     """A call whose rows fit one block writes dgamma itself, four columns a
     store when its outputs allow; outputs that are only element-aligned take
