@@ -1018,19 +1018,24 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
     if ((a.dres || (B16 && a.layer)) && p.vec == VW && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
         (int64_t)a.N <= (int64_t)3 * RMSN_TPR_MAX * VW)
         return launch_bwd_cfg<DT, VW, RMSN_TPR_MAX, 3, false, B16>(a, grid, s);
-    // Longer 16-bit rows of the fused backward (12296-16384 elements) keep
-    // four chunks a thread and one window; from RMSN_FUSED_CAP_MIN_M rows on
-    // the long-row kernel, which holds the block's next row in flight while
-    // it computes the current one (its dgamma accumulators in LDS leave the
-    // registers for two rows), runs them faster. Measured on MI355X, µs per
-    // call: bf16 16384 x 16384 384.2 -> 356.0, 16384 x 14336 359.2 -> 315.1,
-    // 4096 x 12296 94.9 -> 84.8, f16 4096 x 16384 107.3 -> 100.7; but 2048 x
-    // 16384 59.5 -> 60.2 and 1024 x 16384 34.6 -> 38.0, so fewer rows stay
-    // here. The plain backward (two windows already) gains nothing there
-    // (16384 x 16384 300.0 -> 305.9) and LayerNorm, with the next row loaded
-    // as well, loses (16384 x 16384 294.3 -> 317.8).
-    if (B16 && a.dres && p.vec == VW && p.tpr == RMSN_TPR_MAX && p.k == 4 && a.M >= RMSN_FUSED_CAP_MIN_M)
-        return launch_bwd_fused_next_row(DT, a, grid, s);
+    // Longer 16-bit rows (12296-16384 elements) keep four chunks a thread
+    // and, for the fused and LayerNorm backwards, one window. The long-row
+    // kernel, which keeps its dgamma accumulators in LDS and so holds the
+    // block's next row in flight while it computes the current one, runs
+    // them faster: measured on MI355X, µs per call, fused bf16 16384 x 14336
+    // 359.2 -> 315.1, 4096 x 12296 94.9 -> 84.8, 2048 x 16384 58.3 -> 55.1,
+    // 512 x 16384 22.2 -> 20.4; LayerNorm bf16 4096 x 14336 80.1 -> 72.6,
+    // 16384 x 12296 287.2 -> 271.4, 1024 x 16384 36.5 -> 34.3, f16 4096 x
+    // 16384 88.9 -> 81.4. LayerNorm rows of exactly 16384 elements lost there
+    // at many rows (6144 x 16384 124.0 -> 128.4, 16384 x 16384 297 -> 324)
+    // and keep the main kernel above 2^26 elements a call; the plain
+    // backward (two windows already) gains nothing (16384 x 16384 298 ->
+    // 310, 4096 x 14336 63.5 -> 62.4) and stays.
+    if (B16 && p.vec == VW && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
+        (int64_t)a.N > (int64_t)3 * RMSN_TPR_MAX * VW &&
+        (a.dres || (a.layer && ((int64_t)a.N < (int64_t)4 * RMSN_TPR_MAX * VW ||
+                                a.M * (int64_t)a.N <= ((int64_t)1 << 26)))))
+        return launch_bwd_next_row(DT, a, grid, s);
     return dispatch<BwdLaunch, DT>(p, a, grid, s);
 }
 

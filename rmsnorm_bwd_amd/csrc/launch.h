@@ -59,9 +59,10 @@ hipError_t launch_fwd(int dtype, const RowPlan &p, const FwdArgs &a, int grid, h
 // (p.long_row): long_rows.hip.
 hipError_t launch_bwd_long(int dtype, const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s);
 hipError_t launch_fwd_long(int dtype, const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s);
-// The fused backward (a.dres set) of 16-bit rows on 16-byte chunks, four a
-// thread of 512 (at most 16384 elements), by the long-row kernel that loads
-// a block's next row during the current one: long_rows.hip.
-hipError_t launch_bwd_fused_next_row(int dtype, const BwdArgs &a, int grid, hipStream_t s);
+// The fused (a.dres set) or LayerNorm (a.layer) backward of 16-bit rows on
+// 16-byte chunks, four a thread of 512 (at most 16384 elements), by the
+// long-row kernel that loads a block's next row during the current one:
+// long_rows.hip. Other calls fail with hipErrorInvalidValue.
+hipError_t launch_bwd_next_row(int dtype, const BwdArgs &a, int grid, hipStream_t s);
 
 }  // namespace rmsn

@@ -1,8 +1,8 @@
 // long_rows.hip - forward and backward for rows of more than 16384
 // elements (up to MAX_N), where a row no longer fits the register-resident
 // window ring of kernels.hip next to the weight-gradient accumulators; also
-// the fused backward of 16-bit rows of 12296-16384 elements at 4096 rows and
-// more, where that ring holds only one window.
+// the fused and (mostly) the LayerNorm backward of 16-bit rows of
+// 12296-16384 elements, where that ring holds only one window.
 //
 // Pages cited, by title:
 //   [I769] FlyDSL issue #769, "[Feature] Add rmsnorm backward (+ forward saves
@@ -20,8 +20,8 @@
 // One row per block of 512 threads at a time; each thread owns the chunks t,
 // t + 512, ... (K of them, VEC elements each, K * VEC = 64), so a row of up
 // to 32768 elements is covered (fewer chunks where the plan gives fewer:
-// six for 16-bit rows of at most 24576 elements, four for the fused rows of
-// at most 16384). Persistent grid: block b takes rows b, b + G,
+// six for 16-bit rows of at most 24576 elements, four for the fused and
+// LayerNorm rows of at most 16384). Persistent grid: block b takes rows b, b + G,
 // ... Row tensors go through buffer descriptors whose range is the row, so
 // chunks past the row end read as zero and are not stored.
 //
@@ -325,7 +325,9 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
     constexpr bool FUSED = OP == OPL_FUSED, LN = OP == OPL_LN;
     constexpr int ES = ElemSize<DT>::value;
     constexpr bool GRES = MODE != LM_RELOAD;  // gamma resident in registers
-    static_assert(MODE != LM_PREFETCH || (ES == 2 && !LN), "two rows fit beside gamma for 16-bit RMSNorm only");
+    // two rows fit beside gamma for 16-bit types, beside LayerNorm's dbeta
+    // accumulators too at four chunks a thread
+    static_assert(MODE != LM_PREFETCH || (ES == 2 && (!LN || K * VEC <= 32)), "two rows do not fit");
     static_assert((LG * VEC) % 4 == 0 && K % LG == 0, "whole accumulator slots per group");
     static_assert(K % 2 == 0, "gamma fenced in pairs of chunks");
     // slot s of thread t at acc_lds[s][t]: consecutive lanes, consecutive 16 bytes
@@ -387,8 +389,8 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
     auto load_rstd = [&](int64_t row, uint32_t nr) -> float {
         return buf_load_f32(make_rsrc(at(a.rstd, row, 4), nr * 4u), 0u);
     };
-    auto load_mean = [&](int64_t row) -> float {
-        if constexpr (LN) return buf_load_f32(make_rsrc(at(a.mean, row, 4), 4u), 0u);
+    auto load_mean = [&](int64_t row, uint32_t nr) -> float {
+        if constexpr (LN) return buf_load_f32(make_rsrc(at(a.mean, row, 4), nr * 4u), 0u);
         return 0.f;
     };
     auto load_dres = [&](int64_t row, P (&zv)[FUSED ? K : 1]) {
@@ -466,19 +468,22 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
         int64_t row = blockIdx.x;  // < M: the grid has at most M blocks
         load_row(row, 1u, xa, da);
         float ra = load_rstd(row, 1u), rb;
+        float ma = load_mean(row, 1u), mb;
         for (;;) {
             const uint32_t nb = row + G < M ? 1u : 0u;
             load_dres(row, z);
             load_row(row + G, nb, xb, db);
             rb = load_rstd(row + G, nb);
-            process(row, xa, da, z, ra, 0.f);
+            mb = load_mean(row + G, nb);
+            process(row, xa, da, z, ra, ma);
             row += G;
             if (row >= M) break;
             const uint32_t na = row + G < M ? 1u : 0u;
             load_dres(row, z);
             load_row(row + G, na, xa, da);
             ra = load_rstd(row + G, na);
-            process(row, xb, db, z, rb, 0.f);
+            ma = load_mean(row + G, na);
+            process(row, xb, db, z, rb, mb);
             row += G;
             if (row >= M) break;
         }
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(LB) void bwd_long_1pass_kernel(BwdArgs a) {
             load_row(row, 1u, xv, dv);
             load_dres(row, zv);
             const float r = load_rstd(row, 1u);
-            process(row, xv, dv, zv, r, load_mean(row));
+            process(row, xv, dv, zv, r, load_mean(row, 1u));
         }
     }
     // this block's weight-gradient sums (dgamma from its own LDS slots: no
@@ -730,11 +735,20 @@ hipError_t launch_bwd_long(int dtype, const RowPlan &p, const BwdArgs &a, int gr
     }
 }
 
-hipError_t launch_bwd_fused_next_row(int dtype, const BwdArgs &a, int grid, hipStream_t s) {
-    if (!a.dres) return hipErrorInvalidValue;
+template <int DT>
+hipError_t bwd_next_row_dt(const BwdArgs &a, int grid, hipStream_t s) {
+    if (a.layer) {
+        hipLaunchKernelGGL((bwd_long_1pass_kernel<DT, 8, 4, OPL_LN, LM_PREFETCH>), dim3(grid), dim3(LB), 0, s, a);
+        return hipGetLastError();
+    }
+    if (a.dres) return bwd_long_rms<DT, 8, 4, OPL_FUSED>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_next_row(int dtype, const BwdArgs &a, int grid, hipStream_t s) {
     switch (dtype) {
-    case DT_F16: return bwd_long_rms<DT_F16, 8, 4, OPL_FUSED>(a, grid, s);
-    case DT_BF16: return bwd_long_rms<DT_BF16, 8, 4, OPL_FUSED>(a, grid, s);
+    case DT_F16: return bwd_next_row_dt<DT_F16>(a, grid, s);
+    case DT_BF16: return bwd_next_row_dt<DT_BF16>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

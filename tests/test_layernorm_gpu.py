@@ -47,7 +47,11 @@ CASES = [
     ("300x10240_bf16", 300, 10240, "bf16", 1e-6),  # three chunks a thread
     ("129x12288_f16", 129, 12288, "f16", 1e-6),  # three chunks a thread, the longest such row
     ("65x4100_f32", 65, 4100, "f32", 1e-6),  # fp32 LayerNorm keeps four chunks a thread here
-    ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread
+    ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread, next-row kernel
+    ("4099x12296_bf16", 4099, 12296, "bf16", 1e-6),  # next-row kernel, ragged M
+    ("300x16384_f16", 300, 16384, "f16", 1e-6),  # full rows, next-row kernel (M * N <= 2^26)
+    ("4100x16384_bf16", 4100, 16384, "bf16", 1e-6),  # full rows past 2^26 elements: main kernel
+    ("65x14336_bf16", 65, 14336, "bf16", 1e-6),  # next-row kernel, fewer rows than blocks
 ]
 
 
@@ -136,6 +140,12 @@ def test_layernorm_deterministic_repeats_bit_for_bit():
 def test_layernorm_atomic_mode_within_tolerance():
     print("case layernorm atomic", flush=True)
     check(run_case(1024, 4096, "bf16", 1e-6, flags=R.DGAMMA_ATOMIC))
+
+
+@pytest.mark.parametrize("flags", [R.DGAMMA_DETERMINISTIC, R.DGAMMA_ATOMIC, R.DGAMMA_ONE_BLOCK])
+def test_layernorm_next_row_kernel_every_dgamma_mode(flags):
+    print("case layernorm next-row kernel, mode", flags, flush=True)
+    check(run_case(130, 14336, "bf16", 1e-6, flags=flags))
 
 
 # (1100, 24576): several rows a block through the one-read kernel

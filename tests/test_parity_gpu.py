@@ -278,11 +278,12 @@ def test_fused_three_chunk_rows(M, N, dt):
     check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M + 7 * N)))
 
 
-# From 4096 rows the fused backward runs 16-bit rows of 12296-16384 elements
-# on the long-row kernel, which loads a block's next row during the current
-# one: ragged M on the capped grid, both 16-bit types, both ends of the range
-# (2048 rows stay on the main kernel).
-FUSED_NEXT_ROW = [(4099, 12296, "bf16"), (4096, 16384, "f16"), (4100, 14336, "bf16"), (2048, 16384, "bf16")]
+# The fused backward runs 16-bit rows of 12296-16384 elements on the
+# long-row kernel, which loads a block's next row during the current one:
+# ragged M on the capped grid and below it, both 16-bit types, both ends of
+# the range, fewer rows than blocks.
+FUSED_NEXT_ROW = [(4099, 12296, "bf16"), (4096, 16384, "f16"), (4100, 14336, "bf16"), (2048, 16384, "bf16"),
+                  (300, 12296, "f16"), (33, 16384, "bf16")]
 
 
 @pytest.mark.parametrize("M,N,dt", FUSED_NEXT_ROW)

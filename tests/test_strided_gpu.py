@@ -146,7 +146,10 @@ def test_forward_strided(name, M, N, dt, pads):
         assert gaps_untouched(buf, N)
 
 
-@pytest.mark.parametrize("name,M,N,dt,pads", BWD_CASES[:5], ids=[c[0] for c in BWD_CASES[:5]])
+LN_CASES = BWD_CASES[:5] + [("300x14336_bf16_next_row", 300, 14336, "bf16", (8, 16, 24, 8))]
+
+
+@pytest.mark.parametrize("name,M,N,dt,pads", LN_CASES, ids=[c[0] for c in LN_CASES])
 def test_layernorm_strided(name, M, N, dt, pads):
     print("case strided layernorm", name, flush=True)
     td = T[dt]
