@@ -39,7 +39,11 @@
 // RMSNorm the block's next row is loaded during the current one (the modes
 // of long_mode in plan.h). LayerNorm's dbeta accumulators (a second array
 // would not fit the LDS) stay in registers, which leaves room beside them
-// for a 16-bit row and gamma only.
+// for a 16-bit row and gamma only, or for two rows at four chunks a thread
+// (the rows of at most 16384 elements this kernel takes from kernels.hip).
+// Each thread's sums leave as 16-byte partial stores (or, when one block
+// runs the call, as the gradients themselves, four columns a store where
+// the outputs are aligned for it).
 //
 // Backward in two passes (LayerNorm on fp32 rows, and every variant on
 // single elements, where N or the pointers are not 16-byte aligned): the
