@@ -168,27 +168,6 @@ int bwd_common(const void *x, int64_t ldx, const void *gamma, const void *dy, in
     return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP;
 }
 
-// Blocks for the forward: at most 512, each walking rows with a stride of
-// the grid, so any M is covered and a block holds several windows in its
-// ring. Measured on MI355X against the earlier cap of 2048 (one or two rows
-// a block): fused-add 1024 x 8192 bf16 15.5 -> 12.4 us, 32768 x 8192
-// 415 -> 373 us, LayerNorm 4096 x 4096 16.1 -> 14.9 us, the plain forward
-// unchanged; 384 and 768 lose where rows do not split evenly. The fused-add
-// forward (two row reads, two row writes) on the window ring runs at most
-// 256 from 1024 row windows and 2^23 elements on: bf16 1024 x 8192
-// 12.2-12.3 -> 11.8-11.9 us, 4096 x 4096 25.0-25.2 -> 24.0-24.3 us,
-// 16384 x 1024 25.3-25.5 -> 24.4-24.5 us, 16384 x 2048 49.0-49.5 ->
-// 45.5-45.9 us, 32768 x 8192 368-376 -> 363-375 us. Smaller calls are
-// faster with more blocks (4096 x 1024 7.4-7.6 against 7.9 us with 256,
-// 512 x 4096 4.8 against 5.2 us), and the plain forward loses with 256
-// (4096 x 4096 13.9 -> 15.6 us), LayerNorm more (15.0 -> 19.2 us).
-int64_t fwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool fused) {
-    int64_t steps = (M + p.rpb - 1) / p.rpb;
-    const bool narrow = fused && !p.long_row && steps >= 1024 && M * N >= (int64_t(1) << 23);
-    const int64_t cap = narrow ? 256 : 512;
-    if (steps < 1) steps = 1;
-    return steps < cap ? steps : cap;
-}
 
 // Forward of RMSNorm (plain or fused-add) or, with `layer`, LayerNorm (beta
 // nullable, mean saved).
@@ -230,7 +209,7 @@ int fwd_common(const void *x, int64_t ldx, const void *residual, int64_t ldres, 
     a.ldy = ldy;
     a.ldres_out = ldres_out;
     a.eps = eps;
-    hipError_t e = rmsn::launch_fwd(dtype, p, a, (int)fwd_blocks(M, N, p, fused && !layer),
+    hipError_t e = rmsn::launch_fwd(dtype, p, a, (int)rmsn::fwd_blocks(M, N, p, fused && !layer),
                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP;
 }

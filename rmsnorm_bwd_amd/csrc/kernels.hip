@@ -996,47 +996,40 @@ template <int DT, int VEC, int TPR, int K> struct FwdLaunch {
     }
 };
 
-// The fused and LayerNorm backwards hold more per chunk in their ring
-// (dresidual_out; the dbeta accumulators), so rows of four 16-byte chunks a
-// thread leave them one window in flight. For rows of at most three chunks'
-// worth (1025-1536 chunks: 8200-12288 16-bit or 4100-6144 fp32 elements)
-// the fused backward, and the 16-bit LayerNorm one, take three chunks a
-// thread instead, which leaves room for two windows; the grid, the row
-// plan's other fields and the workspace are unchanged. Measured on MI355X,
-// µs per call: fused bf16 16384 x 10240 286.9 -> 225.7, 16384 x 12288
-// 310.5 -> 271.1, 4096 x 12288 86.9 -> 74.3; fused fp32 16384 x 6144
-// 281.6 -> 263.4, 4096 x 5120 68.8 -> 59.4; LayerNorm bf16 16384 x 12288
-// 230.3 -> 211.9, 4096 x 10240 65.3 -> 54.1. LayerNorm fp32 was mixed
-// (16384 x 6144 200.5 -> 209.0, 4096 x 5120 48.6 -> 47.4) and the plain
-// backward, two windows at four chunks already, slower (bf16 16384 x 12288
-// 202.0 -> 222.5): both keep four.
+// Rows of four 16-byte chunks a thread on 512-thread groups leave the fused
+// backward (dresidual_out in its ring) and LayerNorm's (its dbeta
+// accumulators) one window in flight; bwd_route (plan.h) hands them to
+// other kernels:
+// - three chunks a thread, for rows of at most 1536 chunks (8200-12288
+//   16-bit or 4100-6144 fp32 elements), which leaves room for two windows.
+//   Measured on MI355X, µs per call: fused bf16 16384 x 10240 286.9 ->
+//   225.7, 16384 x 12288 310.5 -> 271.1, 4096 x 12288 86.9 -> 74.3; fused
+//   fp32 16384 x 6144 281.6 -> 263.4, 4096 x 5120 68.8 -> 59.4; LayerNorm
+//   bf16 16384 x 12288 230.3 -> 211.9, 4096 x 10240 65.3 -> 54.1. LayerNorm
+//   fp32 was mixed (16384 x 6144 200.5 -> 209.0, 4096 x 5120 48.6 -> 47.4)
+//   and the plain backward, two windows at four chunks already, slower (bf16
+//   16384 x 12288 202.0 -> 222.5): both keep four.
+// - the long-row kernel, for 16-bit rows of 1537-2048 chunks (12296-16384
+//   elements): it keeps its dgamma accumulators in LDS and so holds the
+//   block's next row in flight while it computes the current one. Measured,
+//   µs per call: fused bf16 16384 x 14336 359.2 -> 315.1, 4096 x 12296
+//   94.9 -> 84.8, 2048 x 16384 58.3 -> 55.1, 512 x 16384 22.2 -> 20.4;
+//   LayerNorm bf16 4096 x 14336 80.1 -> 72.6, 16384 x 12296 287.2 -> 271.4,
+//   1024 x 16384 36.5 -> 34.3, f16 4096 x 16384 88.9 -> 81.4. LayerNorm rows
+//   of exactly 16384 elements lost there at many rows (6144 x 16384 124.0
+//   -> 128.4, 16384 x 16384 297 -> 324) and keep this kernel above 2^26
+//   elements a call; the plain backward gains nothing (16384 x 16384 298 ->
+//   310, 4096 x 14336 63.5 -> 62.4) and stays.
 template <int DT>
 static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_bwd_long(DT, p, a, grid, s);
     constexpr int VW = 16 / ElemSize<DT>::value;
     constexpr bool B16 = VW == 8;  // 16-bit elements
-    if ((a.dres || (B16 && a.layer)) && p.vec == VW && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
-        (int64_t)a.N <= (int64_t)3 * RMSN_TPR_MAX * VW)
-        return launch_bwd_cfg<DT, VW, RMSN_TPR_MAX, 3, false, B16>(a, grid, s);
-    // Longer 16-bit rows (12296-16384 elements) keep four chunks a thread
-    // and, for the fused and LayerNorm backwards, one window. The long-row
-    // kernel, which keeps its dgamma accumulators in LDS and so holds the
-    // block's next row in flight while it computes the current one, runs
-    // them faster: measured on MI355X, µs per call, fused bf16 16384 x 14336
-    // 359.2 -> 315.1, 4096 x 12296 94.9 -> 84.8, 2048 x 16384 58.3 -> 55.1,
-    // 512 x 16384 22.2 -> 20.4; LayerNorm bf16 4096 x 14336 80.1 -> 72.6,
-    // 16384 x 12296 287.2 -> 271.4, 1024 x 16384 36.5 -> 34.3, f16 4096 x
-    // 16384 88.9 -> 81.4. LayerNorm rows of exactly 16384 elements lost there
-    // at many rows (6144 x 16384 124.0 -> 128.4, 16384 x 16384 297 -> 324)
-    // and keep the main kernel above 2^26 elements a call; the plain
-    // backward (two windows already) gains nothing (16384 x 16384 298 ->
-    // 310, 4096 x 14336 63.5 -> 62.4) and stays.
-    if (B16 && p.vec == VW && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
-        (int64_t)a.N > (int64_t)3 * RMSN_TPR_MAX * VW &&
-        (a.dres || (a.layer && ((int64_t)a.N < (int64_t)4 * RMSN_TPR_MAX * VW ||
-                                a.M * (int64_t)a.N <= ((int64_t)1 << 26)))))
-        return launch_bwd_next_row(DT, a, grid, s);
-    return dispatch<BwdLaunch, DT>(p, a, grid, s);
+    switch (bwd_route(ElemSize<DT>::value, a.dres != nullptr, a.layer, p, a.M, a.N)) {
+    case BR_THREE_CHUNKS: return launch_bwd_cfg<DT, VW, RMSN_TPR_MAX, 3, false, B16>(a, grid, s);
+    case BR_NEXT_ROW: return launch_bwd_next_row(DT, a, grid, s);
+    default: return dispatch<BwdLaunch, DT>(p, a, grid, s);
+    }
 }
 
 template <int DT>

@@ -209,6 +209,53 @@ inline int long_mode(int esize, bool fused, int64_t M, int64_t N) {
     return fused ? LM_RELOAD : LM_RESIDENT;
 }
 
+// The backward kernel a row of four 16-byte chunks a thread on a 512-thread
+// group (1025-2048 chunks) runs on, by variant (`fused`: the fused backward
+// with a dresidual_out; the measurements are at dispatch_bwd in
+// kernels.hip):
+//   BR_THREE_CHUNKS  three chunks a thread, for rows of at most 1536 chunks
+//                    of the fused backward and the 16-bit LayerNorm one: two
+//                    windows in flight where four chunks leave them one;
+//   BR_NEXT_ROW      the long-row kernel that loads a block's next row during
+//                    the current one (long_rows.hip), for 16-bit rows of
+//                    1537-2048 chunks of the fused backward and of LayerNorm
+//                    (full rows of 16384 elements up to 2^26 elements a call);
+//   BR_PLAN          the row plan as planned (everything else, the plain
+//                    backward always).
+// The grid and the workspace do not depend on the route.
+enum : int { BR_PLAN = 0, BR_THREE_CHUNKS = 1, BR_NEXT_ROW = 2 };
+inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
+    const int vw = 16 / esize;
+    if (p.long_row || p.vec != vw || p.tpr != RMSN_TPR_MAX || p.k != 4) return BR_PLAN;
+    const bool b16 = esize == 2;
+    if (N <= (int64_t)3 * RMSN_TPR_MAX * vw) return fused || (b16 && layer) ? BR_THREE_CHUNKS : BR_PLAN;
+    const bool full = N == (int64_t)4 * RMSN_TPR_MAX * vw;
+    if (b16 && (fused || (layer && (!full || M * N <= (int64_t(1) << 26))))) return BR_NEXT_ROW;
+    return BR_PLAN;
+}
+
+// Blocks for the forward: at most 512, each walking rows with a stride of
+// the grid, so any M is covered and a block holds several windows in its
+// ring. Measured on MI355X against the earlier cap of 2048 (one or two rows
+// a block): fused-add 1024 x 8192 bf16 15.5 -> 12.4 us, 32768 x 8192
+// 415 -> 373 us, LayerNorm 4096 x 4096 16.1 -> 14.9 us, the plain forward
+// unchanged; 384 and 768 lose where rows do not split evenly. The fused-add
+// forward (two row reads, two row writes) on the window ring runs at most
+// 256 from 1024 row windows and 2^23 elements on: bf16 1024 x 8192
+// 12.2-12.3 -> 11.8-11.9 us, 4096 x 4096 25.0-25.2 -> 24.0-24.3 us,
+// 16384 x 1024 25.3-25.5 -> 24.4-24.5 us, 16384 x 2048 49.0-49.5 ->
+// 45.5-45.9 us, 32768 x 8192 368-376 -> 363-375 us. Smaller calls are
+// faster with more blocks (4096 x 1024 7.4-7.6 against 7.9 us with 256,
+// 512 x 4096 4.8 against 5.2 us), and the plain forward loses with 256
+// (4096 x 4096 13.9 -> 15.6 us), LayerNorm more (15.0 -> 19.2 us).
+inline int64_t fwd_blocks(int64_t M, int64_t N, const RowPlan &p, bool fused) {
+    int64_t steps = (M + p.rpb - 1) / p.rpb;
+    const bool narrow = fused && !p.long_row && steps >= 1024 && M * N >= (int64_t(1) << 23);
+    const int64_t cap = narrow ? 256 : 512;
+    if (steps < 1) steps = 1;
+    return steps < cap ? steps : cap;
+}
+
 // dgamma combining modes actually run.
 enum : int { DG_DIRECT = 0, DG_PARTIAL = 1, DG_ATOMIC = 2 };
 

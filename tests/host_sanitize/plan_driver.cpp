@@ -109,6 +109,44 @@ int main() {
             CHECK(long_mode(4, false, M, N) == LM_RESIDENT, "plain fp32 long rows: gamma not resident");
             CHECK(long_mode(4, true, M, N) == LM_RELOAD, "fused fp32 long rows: gamma does not fit");
         }
+    // The backward's route for four-chunk rows: never for the plain backward;
+    // three chunks a thread cover the row; the next-row kernel (four chunks
+    // of 512 threads) only for 16-bit rows it covers and the three-chunk
+    // plan does not.
+    for (int esize : {2, 4})
+        for (int64_t N = 1; N <= MAX_N; ++N) {
+            if (!plan_rows(N, esize, true, &p)) continue;
+            for (int64_t M : {int64_t(1), int64_t(300), int64_t(4096), int64_t(4100), int64_t(1) << 20})
+                for (int v = 0; v < 3; ++v) {
+                    const bool fused = v == 1, layer = v == 2;
+                    const int r = bwd_route(esize, fused, layer, p, M, N);
+                    CHECK(v != 0 || r == BR_PLAN, "plain backward routed at N = %lld", (long long)N);
+                    if (r == BR_THREE_CHUNKS)
+                        CHECK(p.k == 4 && p.tpr == 512 && (int64_t)3 * p.tpr * p.vec >= N && p.vec * esize == 16 &&
+                                  (fused || esize == 2),
+                              "three-chunk route at N = %lld esize %d", (long long)N, esize);
+                    if (r == BR_NEXT_ROW)
+                        CHECK(esize == 2 && p.vec == 8 && p.k == 4 && N > 12288 && N <= 16384 && !p.long_row,
+                              "next-row route at N = %lld", (long long)N);
+                    // the rows the measurements chose for each route take it
+                    if (esize == 2 && p.vec == 8 && N > 8192 && N <= 12288 && (fused || layer))
+                        CHECK(r == BR_THREE_CHUNKS, "16-bit N = %lld not on three chunks", (long long)N);
+                    if (esize == 2 && p.vec == 8 && N > 12288 && N < 16384 && (fused || layer))
+                        CHECK(r == BR_NEXT_ROW, "16-bit N = %lld not on the next-row kernel", (long long)N);
+                }
+            // the forward's grid: at least one block, at most one per row
+            // window and 512, the fused forward's smaller cap only on the
+            // window ring
+            for (int64_t M : {int64_t(0), int64_t(1), int64_t(511), int64_t(4096), int64_t(1) << 20})
+                for (bool fused : {false, true}) {
+                    const int64_t G = fwd_blocks(M, N, p, fused);
+                    const int64_t steps = (M + p.rpb - 1) / p.rpb;
+                    CHECK(G >= 1 && G <= 512 && (steps < 1 || G <= steps), "forward grid %lld at M %lld N %lld",
+                          (long long)G, (long long)M, (long long)N);
+                    if (!fused || p.long_row) CHECK(G == (steps < 1 ? 1 : (steps < 512 ? steps : 512)),
+                                                    "forward grid %lld off the 512 cap", (long long)G);
+                }
+        }
     std::printf("plan driver: %d failed checks\n", failures);
     return failures ? 1 : 0;
 }
