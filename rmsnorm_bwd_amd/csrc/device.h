@@ -129,15 +129,19 @@ constexpr int RSRC_WORD3 = 0x00020000;
 constexpr uint32_t OOB = 0x80000000u;
 // Cache-policy bits of a buffer access on gfx950 (bit 0 SC0, bit 1 NT,
 // bit 4 SC1). NT marks data streamed once; SC1 marks a store system-coherent.
-// The streamed row loads use NT (without it the long runs lose 7%). A kernel
-// with a single streamed output (the plain and LayerNorm dx, and their
-// forwards' y) stores it with SC1; the fused-add kernels store with NT.
-// Measured on MI355X: SC1 takes the plain backward at 4096 x 4096 bf16 from
-// 23.0 to 22.2 us and at 16384 x 4096 from 69.5 to 65.5 us, the plain
-// forward at 16384 x 4096 from 48 to 42 us and the LayerNorm forward at
-// 4096 x 4096 from 14.9 to 14.3 us; the fused backward runs 0.7 us slower
-// with it at 1024 x 8192 and the fused forward 1 us slower there and 6%
-// slower at 32768 x 8192. All three are build-time knobs.
+// The streamed row loads use NT (without it the long runs lose 7%). The
+// plain and LayerNorm backwards store their single streamed output, dx,
+// with SC1; the fused-add backward and every forward store with NT.
+// Measured on MI355X, bf16: SC1 takes the plain backward at 4096 x 4096
+// from 23.0 to 22.2 us and at 16384 x 4096 from 69.5 to 65.5 us (against
+// default stores; NT there: 4096 x 4096 20.4 -> 21.3 us, 16384 x 8192
+// 121.7 -> 131-137 us against SC1), while the fused backward runs 0.7 us
+// slower with it at 1024 x 8192. The forwards' y is faster with NT than
+// with SC1 at every size measured (plain 4096 x 4096 14.0 -> 13.6 us,
+// 16384 x 8192 93.3 -> 88.8-91.1 us, 32768 x 8192 197.7 -> 184.7 us;
+// LayerNorm 32768 x 8192 202.7 -> 190.6 us), and SC1 faster than default
+// stores (plain 16384 x 4096 48 -> 42 us at the time). All are build-time
+// knobs.
 constexpr int AUX_DEFAULT = 0;
 constexpr int AUX_NT = 2;
 #ifndef RMSN_LOAD_AUX
@@ -149,9 +153,13 @@ constexpr int AUX_NT = 2;
 #ifndef RMSN_SINGLE_STORE_AUX
 #define RMSN_SINGLE_STORE_AUX 16
 #endif
+#ifndef RMSN_FWD_STORE_AUX
+#define RMSN_FWD_STORE_AUX 2
+#endif
 constexpr int AUX_STREAM_LOAD = RMSN_LOAD_AUX;
 constexpr int AUX_STREAM_STORE = RMSN_STORE_AUX;
-constexpr int AUX_SINGLE_STORE = RMSN_SINGLE_STORE_AUX;
+constexpr int AUX_SINGLE_STORE = RMSN_SINGLE_STORE_AUX;  // plain and LayerNorm dx
+constexpr int AUX_FWD_STORE = RMSN_FWD_STORE_AUX;        // the forwards' y
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, RSRC_WORD3);

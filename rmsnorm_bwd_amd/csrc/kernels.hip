@@ -790,7 +790,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
         const uint32_t nr = rows_in<RPB>(wb, M);
         const rsrc_t ry = window_rsrc<ES>(a.y, wb, a.ldy, nr, row_bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(ry, gy + coff[k], yo[k]);
+        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_FWD_STORE>(ry, gy + coff[k], yo[k]);
         if constexpr (FUSED) {
             const rsrc_t ro = window_rsrc<ES>(a.residual_out, wb, a.ldres_out, nr, row_bytes);
 #pragma unroll

@@ -209,8 +209,7 @@ __global__ __launch_bounds__(LB) void fwd_long_kernel(FwdArgs a) {
                     else
                         o[e] = elem(av[k0 + j], e) * r * elem(gv[j], e);
                 }
-                buf_store<DT, VEC, FUSED ? AUX_STREAM_STORE : AUX_SINGLE_STORE>(ry, off(k0 + j),
-                                                                               make_pack<DT, VEC>(o));
+                buf_store<DT, VEC, AUX_FWD_STORE>(ry, off(k0 + j), make_pack<DT, VEC>(o));
             }
         }
     }
