@@ -130,18 +130,25 @@ constexpr uint32_t OOB = 0x80000000u;
 // Cache-policy bits of a buffer access on gfx950 (bit 0 SC0, bit 1 NT,
 // bit 4 SC1). NT marks data streamed once; SC1 marks a store system-coherent.
 // The streamed row loads use NT (without it the long runs lose 7%). The
-// plain and LayerNorm backwards store their single streamed output, dx,
-// with SC1; the fused-add backward and every forward store with NT.
+// main kernel's plain and LayerNorm backwards store their single streamed
+// output, dx, with SC1; the fused-add backward and the long-row backwards
+// store with NT. The plain and LayerNorm forwards store y with SC1 where a
+// thread holds fewer than 16 elements of a row (16-bit rows of at most 4096
+// elements on the vector path) and with NT where it holds more (and in the
+// long-row kernels); the fused forward stores with NT.
 // Measured on MI355X, bf16: SC1 takes the plain backward at 4096 x 4096
 // from 23.0 to 22.2 us and at 16384 x 4096 from 69.5 to 65.5 us (against
 // default stores; NT there: 4096 x 4096 20.4 -> 21.3 us, 16384 x 8192
 // 121.7 -> 131-137 us against SC1), while the fused backward runs 0.7 us
-// slower with it at 1024 x 8192. The forwards' y is faster with NT than
-// with SC1 at every size measured (plain 4096 x 4096 14.0 -> 13.6 us,
-// 16384 x 8192 93.3 -> 88.8-91.1 us, 32768 x 8192 197.7 -> 184.7 us;
-// LayerNorm 32768 x 8192 202.7 -> 190.6 us), and SC1 faster than default
-// stores (plain 16384 x 4096 48 -> 42 us at the time). All are build-time
-// knobs.
+// slower with it at 1024 x 8192. The plain forward's y, NT against SC1,
+// depends on the row length: 1024 x 8192 7.7 -> 6.9-7.1 us, 16384 x 8192
+// 91.6 -> 89.1 us, 32768 x 8192 195 -> 183 us, long rows 128 x 32768 5.9 ->
+// 5.4 us, 4096 x 24576 68.9 -> 66.3 us, the element path 4096 x 4097 25.3
+// -> 22.1 us; but 16384 x 4096 42.3 -> 47.5 us, 16384 x 2048 22.6 -> 25.1
+// us, 32768 x 1024 22.7 -> 25.1 us and 4096 x 4096 12.8 -> 13.3 us with
+// rotated buffer sets of three row arrays (sets of two arrays measured NT
+// up to 3% faster there). SC1 is faster than default stores (plain 16384 x
+// 4096 48 -> 42 us). All are build-time knobs.
 constexpr int AUX_DEFAULT = 0;
 constexpr int AUX_NT = 2;
 #ifndef RMSN_LOAD_AUX
@@ -156,10 +163,14 @@ constexpr int AUX_NT = 2;
 #ifndef RMSN_FWD_STORE_AUX
 #define RMSN_FWD_STORE_AUX 2
 #endif
+#ifndef RMSN_FWD_SHORT_STORE_AUX
+#define RMSN_FWD_SHORT_STORE_AUX 16
+#endif
 constexpr int AUX_STREAM_LOAD = RMSN_LOAD_AUX;
 constexpr int AUX_STREAM_STORE = RMSN_STORE_AUX;
 constexpr int AUX_SINGLE_STORE = RMSN_SINGLE_STORE_AUX;  // plain and LayerNorm dx
-constexpr int AUX_FWD_STORE = RMSN_FWD_STORE_AUX;        // the forwards' y
+constexpr int AUX_FWD_STORE = RMSN_FWD_STORE_AUX;              // the forwards' y
+constexpr int AUX_FWD_SHORT_STORE = RMSN_FWD_SHORT_STORE_AUX;  // y of rows short a thread
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, RSRC_WORD3);

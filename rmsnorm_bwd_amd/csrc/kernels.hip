@@ -786,11 +786,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs a) {
             yo[k] = make_pack<DT, VEC>(o);
         }
     };
+    // y: NT for the fused forward and where a thread holds 16 or more
+    // elements of a row, SC1 below (the measurements are at the cache-policy
+    // bits in device.h)
+    constexpr int Y_STORE = FUSED || K * VEC >= 16 ? AUX_FWD_STORE : AUX_FWD_SHORT_STORE;
     auto store_rows = [&](int64_t wb, const P (&av)[K], const P (&yo)[K]) {
         const uint32_t nr = rows_in<RPB>(wb, M);
         const rsrc_t ry = window_rsrc<ES>(a.y, wb, a.ldy, nr, row_bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k) buf_store<DT, VEC, AUX_FWD_STORE>(ry, gy + coff[k], yo[k]);
+        for (int k = 0; k < K; ++k) buf_store<DT, VEC, Y_STORE>(ry, gy + coff[k], yo[k]);
         if constexpr (FUSED) {
             const rsrc_t ro = window_rsrc<ES>(a.residual_out, wb, a.ldres_out, nr, row_bytes);
 #pragma unroll
