@@ -131,8 +131,8 @@ constexpr uint32_t OOB = 0x80000000u;
 // bit 4 SC1). NT marks data streamed once; SC1 marks a store system-coherent.
 // The streamed row loads use NT (without it the long runs lose 7%). The
 // main kernel's plain and LayerNorm backwards store their single streamed
-// output, dx, with SC1; the fused-add backward and the long-row backwards
-// store with NT. The plain and LayerNorm forwards store y with SC1 where a
+// output, dx, with SC1 on 16-byte chunks; the fused-add backward, the
+// element path and the long-row backwards store with NT. The plain and LayerNorm forwards store y with SC1 where a
 // thread holds fewer than 16 elements of a row (16-bit rows of at most 4096
 // elements on the vector path) and with NT where it holds more (and in the
 // long-row kernels); the fused forward stores with NT.
