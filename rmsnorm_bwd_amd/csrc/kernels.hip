@@ -309,11 +309,15 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             out[k] = make_pack<DT, VEC>(o);
         }
     };
-    // dx: SC1 for the plain and LayerNorm backwards on 16-byte chunks, NT for
-    // the fused backward and on the element path (single elements: NT
-    // measured faster there, 4096 x 12289 bf16 104.0 -> 92.7 us, 600 x 6001
-    // 16.4 -> 14.3 us, LayerNorm 4096 x 4097 45.2 -> 42.3 us)
-    constexpr int DX_STORE = FUSED || VEC == 1 ? AUX_STREAM_STORE : AUX_SINGLE_STORE;
+    // dx: SC1 for the plain backward on 16-byte chunks and for LayerNorm
+    // except on rows of 512 threads that hold 16 or more elements each; NT
+    // for those LayerNorm rows (bf16 1024 x 8192 19.0 -> 17.6 us, 32768 x
+    // 8192 266 -> 255 us; short rows of 16 threads lose with it, 131072 x
+    // 256 37.0 -> 39.1 us), for the fused backward and on the element path
+    // (single elements: 4096 x 12289 bf16 104.0 -> 92.7 us, 600 x 6001 16.4
+    // -> 14.3 us, LayerNorm 4096 x 4097 45.2 -> 42.3 us)
+    constexpr bool LN_NT = LN && TPR == RMSN_TPR_MAX && K * VEC >= 16;
+    constexpr int DX_STORE = FUSED || VEC == 1 || LN_NT ? AUX_STREAM_STORE : AUX_SINGLE_STORE;
     auto store_dx = [&](int64_t wb, const P (&out)[K]) {
         const rsrc_t rw = window_rsrc<ES>(a.dx, wb, a.lddx, rows_in<RPB>(wb, M), row_bytes);
 #pragma unroll
