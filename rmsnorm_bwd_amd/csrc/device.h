@@ -130,11 +130,11 @@ constexpr uint32_t OOB = 0x80000000u;
 // Cache-policy bits of a buffer access on gfx950 (bit 0 SC0, bit 1 NT,
 // bit 4 SC1). NT marks data streamed once; SC1 marks a store system-coherent.
 // The streamed row loads use NT (without it the long runs lose 7%). The
-// main kernel's plain backward stores its single streamed output, dx, with
-// SC1 on 16-byte chunks, and so does LayerNorm's except on rows of 512
-// threads that hold 16 or more elements each; the fused-add backward, those
-// LayerNorm rows, the element path and the long-row backwards store with
-// NT. The
+// main kernel's plain and LayerNorm backwards store their single streamed
+// output, dx, with SC1 on 16-byte chunks, except on rows of 512 threads
+// that hold 16 or more elements each (LayerNorm) or 32 or more 16-bit
+// elements (plain); those rows, the fused-add backward, the element path
+// and the long-row backwards store with NT. The
 // plain and LayerNorm forwards store y with SC1 where a
 // thread holds fewer than 16 elements of a row (16-bit rows of at most 4096
 // elements on the vector path) and with NT where it holds more (and in the
@@ -171,7 +171,7 @@ constexpr int AUX_NT = 2;
 #endif
 constexpr int AUX_STREAM_LOAD = RMSN_LOAD_AUX;
 constexpr int AUX_STREAM_STORE = RMSN_STORE_AUX;
-constexpr int AUX_SINGLE_STORE = RMSN_SINGLE_STORE_AUX;  // plain (and short LayerNorm) dx
+constexpr int AUX_SINGLE_STORE = RMSN_SINGLE_STORE_AUX;  // plain and LayerNorm dx, shorter rows
 constexpr int AUX_FWD_STORE = RMSN_FWD_STORE_AUX;              // the forwards' y
 constexpr int AUX_FWD_SHORT_STORE = RMSN_FWD_SHORT_STORE_AUX;  // y of rows short a thread
 

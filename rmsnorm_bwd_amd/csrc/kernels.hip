@@ -309,15 +309,18 @@ __global__ __launch_bounds__(BLOCK) void bwd_main_kernel(BwdArgs a) {
             out[k] = make_pack<DT, VEC>(o);
         }
     };
-    // dx: SC1 for the plain backward on 16-byte chunks and for LayerNorm
-    // except on rows of 512 threads that hold 16 or more elements each; NT
-    // for those LayerNorm rows (bf16 1024 x 8192 19.0 -> 17.6 us, 32768 x
-    // 8192 266 -> 255 us; short rows of 16 threads lose with it, 131072 x
-    // 256 37.0 -> 39.1 us), for the fused backward and on the element path
-    // (single elements: 4096 x 12289 bf16 104.0 -> 92.7 us, 600 x 6001 16.4
-    // -> 14.3 us, LayerNorm 4096 x 4097 45.2 -> 42.3 us)
-    constexpr bool LN_NT = LN && TPR == RMSN_TPR_MAX && K * VEC >= 16;
-    constexpr int DX_STORE = FUSED || VEC == 1 || LN_NT ? AUX_STREAM_STORE : AUX_SINGLE_STORE;
+    // dx: NT for the fused backward, on the element path (single elements:
+    // 4096 x 12289 bf16 104.0 -> 92.7 us, 600 x 6001 16.4 -> 14.3 us,
+    // LayerNorm 4096 x 4097 45.2 -> 42.3 us) and on rows of 512 threads that
+    // hold 16 or more elements each for LayerNorm (bf16 1024 x 8192 19.0 ->
+    // 17.6 us, 32768 x 8192 266 -> 255 us), 32 or more 16-bit elements for
+    // the plain backward (bf16 16384 x 16384 306 -> 295 us, 1024 x 16384
+    // 27.6 -> 25.8 us); SC1 on the other 16-byte chunks (NT lost there:
+    // plain 16384 x 8192 120 -> 132 us, LayerNorm 131072 x 256 37.0 -> 39.1
+    // us, plain fp32 4096 x 16384 136.5 -> 138.5 us)
+    constexpr bool ROW_NT =
+        TPR == RMSN_TPR_MAX && (LN ? K * VEC >= 16 : ES == 2 && K * VEC >= 32);
+    constexpr int DX_STORE = FUSED || VEC == 1 || ROW_NT ? AUX_STREAM_STORE : AUX_SINGLE_STORE;
     auto store_dx = [&](int64_t wb, const P (&out)[K]) {
         const rsrc_t rw = window_rsrc<ES>(a.dx, wb, a.lddx, rows_in<RPB>(wb, M), row_bytes);
 #pragma unroll
