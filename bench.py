@@ -247,15 +247,17 @@ def mode_sweep(reps=3):
                 torch.cuda.empty_cache()
 
 
-def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 4096, 16384, 32768), dtype="bf16"):
-    """The backward and the forward of plain and fused-add RMSNorm over an
-    (M, N) grid in one dtype: GPU time per call from one HIP-graph replay of
-    `steps` calls rotating over buffer sets of > 512 MiB (as the headline is
-    timed), algorithmic GB/s and its share of 8 TB/s. One JSON line per
-    shape."""
+def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 4096, 16384, 32768), dtype="bf16",
+                ops=("plain", "fused")):
+    """The backward and the forward of plain and fused-add RMSNorm (and, when
+    `ops` names it, LayerNorm) over an (M, N) grid in one dtype: GPU time per
+    call from one HIP-graph replay of `steps` calls rotating over buffer sets
+    of > 512 MiB (as the headline is timed), algorithmic GB/s and its share of
+    8 TB/s. One JSON line per shape."""
     dev = torch.device("cuda:0")
     td = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
-    for op in ("plain", "fused"):
+    for op in ops:
+        ln = op == "layernorm"
         for N in ns:
             for M in ms:
                 w = workloads.custom(op, M, N, dtype, 1e-6, dy_sigma=1e-2)
@@ -265,22 +267,32 @@ def shape_sweep(steps=50, ns=(1024, 2048, 4096, 8192), ms=(1, 128, 512, 1024, 40
                 # cache, as a latency-bound call of that size would in use
                 nsets = max(2, min(steps, -(-ROTATE_BYTES // per)))
                 g = (1 + 0.1 * torch.randn(N, device=dev)).to(td)
+                beta = (0.1 * torch.randn(N, device=dev)).to(td) if ln else None
                 sets = []
                 for _ in range(nsets):
                     x = torch.randn(M, N, device=dev).to(td)
-                    _, rstd = R.rmsnorm_fwd_rstd(x, g, w.eps)
+                    if ln:
+                        _, mean, rstd = R.layernorm_fwd_stats(x, g, beta, w.eps)
+                    else:
+                        mean = None
+                        _, rstd = R.rmsnorm_fwd_rstd(x, g, w.eps)
                     t = dict(x=x, dy=(1e-2 * torch.randn(M, N, device=dev)).to(td),
                              dres=(1e-2 * torch.randn(M, N, device=dev)).to(td)
                              if op == "fused" else None,
-                             rstd=rstd, dx=torch.empty_like(x), dg32=torch.empty(N, device=dev),
+                             rstd=rstd, mean=mean, dx=torch.empty_like(x), dg32=torch.empty(N, device=dev),
                              dg=torch.empty_like(g))
-                    t["ws"] = torch.empty(max(256, R.rmsnorm_bwd_workspace_bytes(M, N, td)),
-                                          dtype=torch.uint8, device=dev)
+                    query = R.layernorm_bwd_workspace_bytes if ln else R.rmsnorm_bwd_workspace_bytes
+                    if ln:
+                        t["db32"], t["db"] = torch.empty(N, device=dev), torch.empty_like(g)
+                    t["ws"] = torch.empty(max(256, query(M, N, td)), dtype=torch.uint8, device=dev)
                     sets.append(t)
 
                 def fwd(t):
                     if op == "plain":
                         R.rmsnorm_fwd_rstd(t["x"], g, w.eps, y=t["dx"], rstd=t["rstd"])
+                    elif ln:
+                        R.layernorm_fwd_stats(t["x"], g, beta, w.eps, y=t["dx"], mean=t["mean"],
+                                              rstd=t["rstd"])
                     else:
                         R.fused_add_rmsnorm_fwd_rstd(t["x"], t["dy"], g, w.eps, out=t["dx"],
                                                      residual_out=t["dres"], rstd=t["rstd"])
@@ -618,7 +630,7 @@ def main():
     ap.add_argument("--mode-sweep", action="store_true",
                     help="time the dgamma modes on an (M, N) grid (one JSON line per shape) and exit")
     ap.add_argument("--shape-sweep", action="store_true",
-                    help="time plain and fused backward and forward on an (M, N) grid "
+                    help="time the backward and forward of --sweep-ops on an (M, N) grid "
                          "(one JSON line per shape) and exit")
     ap.add_argument("--sweep-n", default="1024,2048,4096,8192",
                     help="row lengths of --shape-sweep (comma-separated)")
@@ -626,6 +638,8 @@ def main():
                     help="element type of --shape-sweep")
     ap.add_argument("--sweep-m", default="1,128,512,1024,4096,16384,32768",
                     help="row counts of --shape-sweep (comma-separated)")
+    ap.add_argument("--sweep-ops", default="plain,fused",
+                    help="operations of --shape-sweep (comma-separated: plain, fused, layernorm)")
     ap.add_argument("--api-compare", action="store_true",
                     help="time the backward through autograd against torch's eager RMSNorm on the "
                          "pages' public-API shapes (one JSON line per shape) and exit")
@@ -655,7 +669,8 @@ def main():
         return
     if args.shape_sweep:
         shape_sweep(ns=[int(v) for v in args.sweep_n.split(",")],
-                    ms=[int(v) for v in args.sweep_m.split(",")], dtype=args.sweep_dtype)
+                    ms=[int(v) for v in args.sweep_m.split(",")], dtype=args.sweep_dtype,
+                    ops=args.sweep_ops.split(","))
         return
     if args.floor:
         floor(workloads.WORKLOADS[args.workload])

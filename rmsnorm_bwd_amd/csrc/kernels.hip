@@ -1050,6 +1050,11 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
+    constexpr int VW = 16 / ElemSize<DT>::value;
+    if constexpr (VW == 8) {
+        if (fwd_three_chunks(ElemSize<DT>::value, a.mean != nullptr, p, a.N))
+            return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX, 3>(a, grid, s);
+    }
     return dispatch<FwdLaunch, DT>(p, a, grid, s);
 }
 

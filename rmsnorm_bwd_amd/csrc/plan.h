@@ -234,6 +234,22 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
     return BR_PLAN;
 }
 
+// Whether the LayerNorm forward runs a 16-bit row of 1025-1536 16-byte
+// chunks (8200-12288 elements) on three chunks a thread rather than the
+// plan's four, so that no thread carries an empty chunk slot through its two
+// row passes. Measured on MI355X, GPU time per call, bf16: 4096 x 12288
+// 42.8-43.1 -> 39.6-40.0 us, 1024 x 12288 14.4-14.5 -> 13.1-13.2, 4096 x
+// 10240 39.4 -> 36.2-36.4, 16384 x 12288 142.3-142.7 -> 136.4-136.8, 32768
+// x 12288 277-278 -> 267-268; f16 4096 x 12288 43.5-44.1 -> 39.8-40.2. The
+// plain and fused forwards measured mixed (plain 1024 x 10240 10.6 -> 8.7-9.6
+// us but 16384 x 12288 133.3-133.6 -> 135.6-137.5, fused 16384 x 10240
+// 224.5-225.5 -> 235.5-238.8) and keep the plan.
+inline bool fwd_three_chunks(int esize, bool layer, const RowPlan &p, int64_t N) {
+    const int vw = 16 / esize;
+    return layer && esize == 2 && !p.long_row && p.vec == vw && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
+           N <= (int64_t)3 * RMSN_TPR_MAX * vw;
+}
+
 // Blocks for the forward: at most 512, each walking rows with a stride of
 // the grid, so any M is covered and a block holds several windows in its
 // ring. Measured on MI355X against the earlier cap of 2048 (one or two rows

@@ -134,6 +134,18 @@ int main() {
                     if (esize == 2 && p.vec == 8 && N > 12288 && N < 16384 && (fused || layer))
                         CHECK(r == BR_NEXT_ROW, "16-bit N = %lld not on the next-row kernel", (long long)N);
                 }
+            // the LayerNorm forward's three-chunk route: 16-bit rows of
+            // 8200-12288 elements exactly, which three chunks of 512 threads
+            // cover
+            {
+                CHECK(!fwd_three_chunks(esize, false, p, N), "plain/fused forward on three chunks at N = %lld",
+                      (long long)N);
+                const bool three = fwd_three_chunks(esize, true, p, N);
+                CHECK(three == (esize == 2 && p.vec == 8 && N > 8192 && N <= 12288),
+                      "LayerNorm forward three-chunk route at N = %lld esize %d", (long long)N, esize);
+                if (three) CHECK((int64_t)3 * 512 * p.vec >= N && p.tpr == 512, "three chunks do not cover N = %lld",
+                                 (long long)N);
+            }
             // the forward's grid: at least one block, at most one per row
             // window and 512, the fused forward's smaller cap only on the
             // window ring

@@ -44,8 +44,9 @@ CASES = [
     ("1x4096_bf16", 1, 4096, "bf16", 1e-6),    # one block writes the gradients
     ("150x1500_f16", 150, 1500, "f16", 1e-5),  # element path, 256 threads, 8 elements a thread
     ("200x4097_bf16", 200, 4097, "bf16", 1e-5),  # element path, 512 threads, 16 elements a thread
-    ("300x10240_bf16", 300, 10240, "bf16", 1e-6),  # three chunks a thread
+    ("300x10240_bf16", 300, 10240, "bf16", 1e-6),  # three chunks a thread (backward and forward)
     ("129x12288_f16", 129, 12288, "f16", 1e-6),  # three chunks a thread, the longest such row
+    ("2050x8200_bf16", 2050, 8200, "bf16", 1e-6),  # three chunks a thread, the shortest such row
     ("65x4100_f32", 65, 4100, "f32", 1e-6),  # fp32 LayerNorm keeps four chunks a thread here
     ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread, next-row kernel
     ("4099x12296_bf16", 4099, 12296, "bf16", 1e-6),  # next-row kernel, ragged M

@@ -146,7 +146,8 @@ def test_forward_strided(name, M, N, dt, pads):
         assert gaps_untouched(buf, N)
 
 
-LN_CASES = BWD_CASES[:5] + [("300x14336_bf16_next_row", 300, 14336, "bf16", (8, 16, 24, 8))]
+LN_CASES = BWD_CASES[:5] + [("300x14336_bf16_next_row", 300, 14336, "bf16", (8, 16, 24, 8)),
+                            ("130x10240_bf16_three_chunks", 130, 10240, "bf16", (8, 24, 16, 8))]
 
 
 @pytest.mark.parametrize("name,M,N,dt,pads", LN_CASES, ids=[c[0] for c in LN_CASES])

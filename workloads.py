@@ -102,9 +102,13 @@ def make_inputs(w, M=None, N=None, seed=None):
 
 
 def custom(op, M, N, dtype, eps, seed=0, dy_sigma=1.0):
-    """A workload of the plain or fused kind at an arbitrary shape, for tests."""
+    """A workload of the plain, fused or LayerNorm kind at an arbitrary shape."""
     if op == "plain":
         w = _plain(f"plain_{M}x{N}_{dtype}", M, N, dtype, eps, dy_sigma)
-    else:
+    elif op == "layernorm":
+        w = _layernorm(f"layernorm_{M}x{N}_{dtype}", M, N, dtype, eps)
+    elif op == "fused":
         w = _fused(f"fused_{M}x{N}_{dtype}", M, N, dtype, eps)
+    else:
+        raise ValueError(f"unknown operation {op!r}")
     return Workload(w.name, w.op, w.M, w.N, w.dtype, w.eps, w.dists, seed)
