@@ -1047,6 +1047,9 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
     }
 }
 
+// The LayerNorm forward runs 16-bit rows of 1025-1536 chunks on three chunks
+// a thread (fwd_three_chunks in plan.h, with its measurements); every other
+// forward takes its row plan.
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);

@@ -243,7 +243,8 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 // x 12288 277-278 -> 267-268; f16 4096 x 12288 43.5-44.1 -> 39.8-40.2. The
 // plain and fused forwards measured mixed (plain 1024 x 10240 10.6 -> 8.7-9.6
 // us but 16384 x 12288 133.3-133.6 -> 135.6-137.5, fused 16384 x 10240
-// 224.5-225.5 -> 235.5-238.8) and keep the plan.
+// 224.5-225.5 -> 235.5-238.8) and keep the plan, as do fp32 LayerNorm rows
+// (16384 x 6144 137-140 -> 147-150 us, 8192 x 4100 53.4 -> 58.0 us).
 inline bool fwd_three_chunks(int esize, bool layer, const RowPlan &p, int64_t N) {
     const int vw = 16 / esize;
     return layer && esize == 2 && !p.long_row && p.vec == vw && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
