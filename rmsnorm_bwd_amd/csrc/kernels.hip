@@ -1047,15 +1047,16 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
     }
 }
 
-// The LayerNorm forward runs 16-bit rows of 1025-1536 chunks on three chunks
-// a thread (fwd_three_chunks in plan.h, with its measurements); every other
-// forward takes its row plan.
+// The forward runs 16-bit rows of 1025-1536 chunks on three chunks a thread
+// where fwd_three_chunks (plan.h, with its measurements) says so: LayerNorm's
+// always, the plain and fused forwards' up to 2^26 elements a call; every
+// other forward takes its row plan.
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
     constexpr int VW = 16 / ElemSize<DT>::value;
     if constexpr (VW == 8) {
-        if (fwd_three_chunks(ElemSize<DT>::value, a.mean != nullptr, p, a.N))
+        if (fwd_three_chunks(ElemSize<DT>::value, a.mean != nullptr, p, a.M, a.N))
             return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX, 3>(a, grid, s);
     }
     return dispatch<FwdLaunch, DT>(p, a, grid, s);

@@ -234,21 +234,27 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
     return BR_PLAN;
 }
 
-// Whether the LayerNorm forward runs a 16-bit row of 1025-1536 16-byte
-// chunks (8200-12288 elements) on three chunks a thread rather than the
-// plan's four, so that no thread carries an empty chunk slot through its two
-// row passes. Measured on MI355X, GPU time per call, bf16: 4096 x 12288
+// Whether the forward runs a 16-bit row of 1025-1536 16-byte chunks
+// (8200-12288 elements) on three chunks a thread rather than the plan's
+// four, so that no thread carries an empty chunk slot: LayerNorm's (two row
+// passes) at every size, the plain and fused forwards' up to 2^26 elements a
+// call. Measured on MI355X, GPU time per call, bf16: LayerNorm 4096 x 12288
 // 42.8-43.1 -> 39.6-40.0 us, 1024 x 12288 14.4-14.5 -> 13.1-13.2, 4096 x
 // 10240 39.4 -> 36.2-36.4, 16384 x 12288 142.3-142.7 -> 136.4-136.8, 32768
-// x 12288 277-278 -> 267-268; f16 4096 x 12288 43.5-44.1 -> 39.8-40.2. The
-// plain and fused forwards measured mixed (plain 1024 x 10240 10.6 -> 8.7-9.6
-// us but 16384 x 12288 133.3-133.6 -> 135.6-137.5, fused 16384 x 10240
-// 224.5-225.5 -> 235.5-238.8) and keep the plan, as do fp32 LayerNorm rows
-// (16384 x 6144 137-140 -> 147-150 us, 8192 x 4100 53.4 -> 58.0 us).
-inline bool fwd_three_chunks(int esize, bool layer, const RowPlan &p, int64_t N) {
+// x 12288 277-278 -> 267-268, f16 4096 x 12288 43.5-44.1 -> 39.8-40.2;
+// plain 1024 x 8200 10.5-10.6 -> 8.4-8.5, 2048 x 12288 20.3-20.5 ->
+// 18.1-18.3, 4096 x 10240 32.0-32.6 -> 30.0-30.2, fused 1024 x 12288
+// 18.7-18.9 -> 17.0-17.2, 2048 x 10240 30.5-30.8 -> 28.6-28.7, 4096 x 12288
+// 68.8-69.1 -> 66.3-66.5; but from 8192 x 12288 on the plain and fused
+// forwards lose with it (plain 8192 x 12288 67.5-68.5 -> 68.1-68.5, 16384 x
+// 12288 133.3-133.6 -> 135.6-137.5; fused 8192 x 12288 135.5-138.5 ->
+// 137.4-140.1, 16384 x 10240 224.5-225.5 -> 235.5-238.8). fp32 LayerNorm
+// rows lose too (16384 x 6144 137-140 -> 147-150 us, 8192 x 4100 53.4 ->
+// 58.0 us) and keep the plan.
+inline bool fwd_three_chunks(int esize, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
-    return layer && esize == 2 && !p.long_row && p.vec == vw && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
-           N <= (int64_t)3 * RMSN_TPR_MAX * vw;
+    return esize == 2 && !p.long_row && p.vec == vw && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
+           N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26));
 }
 
 // Blocks for the forward: at most 512, each walking rows with a stride of

@@ -134,18 +134,20 @@ int main() {
                     if (esize == 2 && p.vec == 8 && N > 12288 && N < 16384 && (fused || layer))
                         CHECK(r == BR_NEXT_ROW, "16-bit N = %lld not on the next-row kernel", (long long)N);
                 }
-            // the LayerNorm forward's three-chunk route: 16-bit rows of
-            // 8200-12288 elements exactly, which three chunks of 512 threads
-            // cover
-            {
-                CHECK(!fwd_three_chunks(esize, false, p, N), "plain/fused forward on three chunks at N = %lld",
-                      (long long)N);
-                const bool three = fwd_three_chunks(esize, true, p, N);
-                CHECK(three == (esize == 2 && p.vec == 8 && N > 8192 && N <= 12288),
-                      "LayerNorm forward three-chunk route at N = %lld esize %d", (long long)N, esize);
-                if (three) CHECK((int64_t)3 * 512 * p.vec >= N && p.tpr == 512, "three chunks do not cover N = %lld",
-                                 (long long)N);
-            }
+            // the forward's three-chunk route: 16-bit rows of 8200-12288
+            // elements exactly, which three chunks of 512 threads cover;
+            // LayerNorm's at every M, the others' up to 2^26 elements a call
+            for (int64_t M : {int64_t(1), int64_t(300), int64_t(5461), int64_t(5462), int64_t(8192),
+                              int64_t(1) << 20})
+                for (bool layer : {false, true}) {
+                    const bool three = fwd_three_chunks(esize, layer, p, M, N);
+                    CHECK(three == (esize == 2 && p.vec == 8 && N > 8192 && N <= 12288 &&
+                                    (layer || M * N <= (int64_t(1) << 26))),
+                          "forward three-chunk route at M %lld N %lld esize %d layer %d", (long long)M,
+                          (long long)N, esize, (int)layer);
+                    if (three) CHECK((int64_t)3 * 512 * p.vec >= N && p.tpr == 512,
+                                     "three chunks do not cover N = %lld", (long long)N);
+                }
             // the forward's grid: at least one block, at most one per row
             // window and 512, the fused forward's smaller cap only on the
             // window ring

@@ -278,6 +278,45 @@ def test_fused_three_chunk_rows(M, N, dt):
     check_case(fused_case(workloads.custom("fused", M, N, dt, 1e-6, seed=M + 7 * N)))
 
 
+# The plain and fused forwards run 16-bit rows of 8200-12288 elements on
+# three chunks a thread up to 2^26 elements a call and on the plan's four
+# beyond: 12288-element rows at 5461 rows (2^26 - 4096 elements) and 5462
+# (just past). The first m0 rows are held to the oracle; the rest repeat them
+# down the tensor, and a row's outputs depend on that row and gamma alone, so
+# every repetition must equal its first occurrence bit for bit.
+@pytest.mark.parametrize("op", ["plain", "fused"])
+@pytest.mark.parametrize("M", [5461, 5462])
+def test_forward_three_chunk_size_limit(op, M):
+    N, m0 = 12288, 43
+    _say("case forward three-chunk limit", op, M, N)
+    w = workloads.custom(op, m0, N, "bf16", 1e-6, seed=M + 13)
+    d = workloads.make_inputs(w)
+    reps = -(-M // m0)
+
+    def tile(t):
+        return t.to(DEV).repeat(reps, 1)[:M].contiguous()
+
+    g = d["gamma"].to(DEV)
+    if op == "plain":
+        r_ref, y_ref = oracle.rmsnorm_fwd(d["x"], d["gamma"], w.eps)
+        y, rstd = R.rmsnorm_fwd_rstd(tile(d["x"]), g, w.eps)
+        rows = [("y", y)]
+    else:
+        added, r_ref, y_ref = oracle.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["gamma"], w.eps)
+        y, res_out, rstd = R.fused_add_rmsnorm_fwd_rstd(tile(d["x"]), tile(d["residual"]), g, w.eps)
+        rows = [("out", y), ("residual_out", res_out)]
+        assert torch.equal(res_out[:m0].cpu(), added), "residual_out differs from the rounded sum"
+    torch.cuda.synchronize()
+    assert_close(rows[0][0], y[:m0], y_ref, torch.bfloat16)
+    er = ((rstd[:m0].cpu().double() - r_ref.double()).abs() / r_ref.double().abs()).max().item()
+    assert er <= 1e-5, f"rstd: error {er:.3g}"
+    full = (M // m0) * m0
+    for name, t in rows + [("rstd", rstd)]:
+        v = t[:full].view(M // m0, m0, *t.shape[1:])
+        assert torch.equal(v, v[:1].expand_as(v)), f"{name}: a repetition differs from the first rows"
+        assert torch.equal(t[full:], t[:M - full]), f"{name}: the ragged tail differs from the first rows"
+
+
 # The fused backward runs 16-bit rows of 12296-16384 elements on the
 # long-row kernel, which loads a block's next row during the current one:
 # ragged M on the capped grid and below it, both 16-bit types, both ends of
