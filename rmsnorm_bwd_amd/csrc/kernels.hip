@@ -1047,17 +1047,20 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
     }
 }
 
-// The forward runs 16-bit rows of 1025-1536 chunks on three chunks a thread
-// where fwd_three_chunks (plan.h, with its measurements) says so: LayerNorm's
-// always, the plain and fused forwards' up to 2^26 elements a call; every
-// other forward takes its row plan.
+// The forward's route for 16-bit rows whose plan leaves chunk slots empty
+// (fwd_route in plan.h, with its measurements): three chunks a thread on 512
+// threads, or on 256-thread groups two rows a block; every other forward
+// takes its row plan.
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
     constexpr int VW = 16 / ElemSize<DT>::value;
     if constexpr (VW == 8) {
-        if (fwd_three_chunks(ElemSize<DT>::value, a.mean != nullptr, p, a.M, a.N))
-            return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX, 3>(a, grid, s);
+        switch (fwd_route(ElemSize<DT>::value, a.residual != nullptr, a.mean != nullptr, p, a.M, a.N)) {
+        case FR_THREE_CHUNKS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX, 3>(a, grid, s);
+        case FR_HALF_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 2, 3>(a, grid, s);
+        default: break;
+        }
     }
     return dispatch<FwdLaunch, DT>(p, a, grid, s);
 }

@@ -234,27 +234,49 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
     return BR_PLAN;
 }
 
-// Whether the forward runs a 16-bit row of 1025-1536 16-byte chunks
-// (8200-12288 elements) on three chunks a thread rather than the plan's
-// four, so that no thread carries an empty chunk slot: LayerNorm's (two row
-// passes) at every size, the plain and fused forwards' up to 2^26 elements a
-// call. Measured on MI355X, GPU time per call, bf16: LayerNorm 4096 x 12288
-// 42.8-43.1 -> 39.6-40.0 us, 1024 x 12288 14.4-14.5 -> 13.1-13.2, 4096 x
-// 10240 39.4 -> 36.2-36.4, 16384 x 12288 142.3-142.7 -> 136.4-136.8, 32768
-// x 12288 277-278 -> 267-268, f16 4096 x 12288 43.5-44.1 -> 39.8-40.2;
-// plain 1024 x 8200 10.5-10.6 -> 8.4-8.5, 2048 x 12288 20.3-20.5 ->
-// 18.1-18.3, 4096 x 10240 32.0-32.6 -> 30.0-30.2, fused 1024 x 12288
-// 18.7-18.9 -> 17.0-17.2, 2048 x 10240 30.5-30.8 -> 28.6-28.7, 4096 x 12288
-// 68.8-69.1 -> 66.3-66.5; but from 8192 x 12288 on the plain and fused
-// forwards lose with it (plain 8192 x 12288 67.5-68.5 -> 68.1-68.5, 16384 x
-// 12288 133.3-133.6 -> 135.6-137.5; fused 8192 x 12288 135.5-138.5 ->
-// 137.4-140.1, 16384 x 10240 224.5-225.5 -> 235.5-238.8). fp32 LayerNorm
-// rows lose too (16384 x 6144 137-140 -> 147-150 us, 8192 x 4100 53.4 ->
-// 58.0 us) and keep the plan.
-inline bool fwd_three_chunks(int esize, bool layer, const RowPlan &p, int64_t M, int64_t N) {
+// The forward kernel a 16-bit row whose plan leaves chunk slots empty runs
+// on:
+//   FR_THREE_CHUNKS  three 16-byte chunks a thread on 512 threads for rows of
+//                    1025-1536 chunks (8200-12288 elements; the plan has four
+//                    a thread): LayerNorm's (two row passes) at every size,
+//                    the plain and fused forwards' up to 2^26 elements a call;
+//   FR_HALF_ROWS     three chunks a thread on 256-thread groups, two rows a
+//                    block, for the plain forward's rows of 513-768 chunks
+//                    (4104-6144 elements; the plan has two a thread on 512
+//                    threads) from 4096 rows;
+//   FR_PLAN          the row plan as planned (everything else).
+// Measured on MI355X, GPU time per call, bf16 unless stated:
+//   three chunks: LayerNorm 4096 x 12288 42.8-43.1 -> 39.6-40.0 us, 1024 x
+//   12288 14.4-14.5 -> 13.1-13.2, 4096 x 10240 39.4 -> 36.2-36.4, 16384 x
+//   12288 142.3-142.7 -> 136.4-136.8, 32768 x 12288 277-278 -> 267-268, f16
+//   4096 x 12288 43.5-44.1 -> 39.8-40.2; plain 1024 x 8200 10.5-10.6 ->
+//   8.4-8.5, 2048 x 12288 20.3-20.5 -> 18.1-18.3, 4096 x 10240 32.0-32.6 ->
+//   30.0-30.2, fused 1024 x 12288 18.7-18.9 -> 17.0-17.2, 2048 x 10240
+//   30.5-30.8 -> 28.6-28.7, 4096 x 12288 68.8-69.1 -> 66.3-66.5; but from
+//   8192 x 12288 on the plain and fused forwards lose with it (plain 8192 x
+//   12288 67.5-68.5 -> 68.1-68.5, 16384 x 12288 133.3-133.6 -> 135.6-137.5;
+//   fused 8192 x 12288 135.5-138.5 -> 137.4-140.1, 16384 x 10240
+//   224.5-225.5 -> 235.5-238.8). fp32 LayerNorm rows lose too (16384 x 6144
+//   137-140 -> 147-150 us, 8192 x 4100 53.4 -> 58.0 us).
+//   half rows, plain: 4096 x 5120 16.9-17.0 -> 15.9-16.0 us, 16384 x 5120
+//   59.7-59.9 -> 56.6-56.9, 32768 x 5120 118.0-120.4 -> 112.7-114.0, 4096 x
+//   6144 19.2-19.4 -> 18.2-18.4, 8192 x 4160 26.4-27.0 -> 25.0-25.1, 16384
+//   x 4608 55.0-55.6 -> 51.6-52.3, 4096 x 4104 15.1-15.4 -> 14.5, f16 4096
+//   x 5120 16.8-17.1 -> 15.8-16.0, 8192 x 6144 35.6-35.8 -> 34.6-35.2; below
+//   4096 rows mixed (3072 x 5120 13.8 -> 12.1 but 2048 x 6144 10.1-10.3 ->
+//   10.4-10.7, 1024 x 5120 5.8 -> 6.8-7.0). The fused forward (4096 x 5120
+//   30.4-30.9 -> 28.7-29.1 but 16384 x 6144 131.4-132.3 -> 135.0-135.3) and
+//   LayerNorm's (4096 x 5120 19.6-19.8 -> 20.4-20.8, 1024 x 6144 7.6 -> 8.9)
+//   keep the plan.
+enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2 };
+inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
-    return esize == 2 && !p.long_row && p.vec == vw && p.tpr == RMSN_TPR_MAX && p.k == 4 &&
-           N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26));
+    if (esize != 2 || p.long_row || p.vec != vw || p.tpr != RMSN_TPR_MAX) return FR_PLAN;
+    if (p.k == 4 && N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26)))
+        return FR_THREE_CHUNKS;
+    if (p.k == 2 && N <= (int64_t)3 * (RMSN_TPR_MAX / 2) * vw && !fused && !layer && M >= 4096)
+        return FR_HALF_ROWS;
+    return FR_PLAN;
 }
 
 // Blocks for the forward: at most 512, each walking rows with a stride of

@@ -134,19 +134,30 @@ int main() {
                     if (esize == 2 && p.vec == 8 && N > 12288 && N < 16384 && (fused || layer))
                         CHECK(r == BR_NEXT_ROW, "16-bit N = %lld not on the next-row kernel", (long long)N);
                 }
-            // the forward's three-chunk route: 16-bit rows of 8200-12288
-            // elements exactly, which three chunks of 512 threads cover;
-            // LayerNorm's at every M, the others' up to 2^26 elements a call
-            for (int64_t M : {int64_t(1), int64_t(300), int64_t(5461), int64_t(5462), int64_t(8192),
-                              int64_t(1) << 20})
-                for (bool layer : {false, true}) {
-                    const bool three = fwd_three_chunks(esize, layer, p, M, N);
-                    CHECK(three == (esize == 2 && p.vec == 8 && N > 8192 && N <= 12288 &&
-                                    (layer || M * N <= (int64_t(1) << 26))),
-                          "forward three-chunk route at M %lld N %lld esize %d layer %d", (long long)M,
-                          (long long)N, esize, (int)layer);
-                    if (three) CHECK((int64_t)3 * 512 * p.vec >= N && p.tpr == 512,
-                                     "three chunks do not cover N = %lld", (long long)N);
+            // the forward's route: three chunks of 512 threads for 16-bit rows
+            // of 8200-12288 elements exactly (LayerNorm's at every M, the
+            // others' up to 2^26 elements a call); three chunks of 256-thread
+            // groups for the plain forward's 16-bit rows of 4104-6144
+            // elements from 4096 rows; in either case the chunks cover the row
+            for (int64_t M : {int64_t(1), int64_t(300), int64_t(4095), int64_t(4096), int64_t(5461), int64_t(5462),
+                              int64_t(8192), int64_t(1) << 20})
+                for (int v = 0; v < 3; ++v) {
+                    const bool fused = v == 1, layer = v == 2;
+                    const int r = fwd_route(esize, fused, layer, p, M, N);
+                    const bool b16v = esize == 2 && p.vec == 8;
+                    CHECK((r == FR_THREE_CHUNKS) ==
+                              (b16v && N > 8192 && N <= 12288 && (layer || M * N <= (int64_t(1) << 26))),
+                          "forward three-chunk route at M %lld N %lld esize %d variant %d", (long long)M,
+                          (long long)N, esize, v);
+                    CHECK((r == FR_HALF_ROWS) == (b16v && N > 4096 && N <= 6144 && v == 0 && M >= 4096),
+                          "forward half-row route at M %lld N %lld esize %d variant %d", (long long)M, (long long)N,
+                          esize, v);
+                    if (r == FR_THREE_CHUNKS)
+                        CHECK((int64_t)3 * 512 * p.vec >= N && p.tpr == 512, "three chunks do not cover N = %lld",
+                              (long long)N);
+                    if (r == FR_HALF_ROWS)
+                        CHECK((int64_t)3 * 256 * p.vec >= N && p.tpr == 512 && p.k == 2,
+                              "half-row chunks do not cover N = %lld", (long long)N);
                 }
             // the forward's grid: at least one block, at most one per row
             // window and 512, the fused forward's smaller cap only on the

@@ -317,6 +317,19 @@ def test_forward_three_chunk_size_limit(op, M):
         assert torch.equal(t[full:], t[:M - full]), f"{name}: the ragged tail differs from the first rows"
 
 
+# The plain forward runs 16-bit rows of 4104-6144 elements on 256-thread
+# groups (three chunks a thread, two rows a block) from 4096 rows: ragged M
+# (an odd last window), both 16-bit types, both ends of the range, and 4095
+# rows (the plan's two chunks on 512 threads). The backward of each runs too.
+HALF_ROWS = [(4096, 5120, "bf16"), (4097, 6144, "f16"), (4101, 4104, "bf16"), (4095, 6144, "bf16")]
+
+
+@pytest.mark.parametrize("M,N,dt", HALF_ROWS)
+def test_plain_forward_half_row_groups(M, N, dt):
+    _say("case plain forward half rows", M, N, dt)
+    check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-6, seed=M + 5 * N)))
+
+
 # The fused backward runs 16-bit rows of 12296-16384 elements on the
 # long-row kernel, which loads a block's next row during the current one:
 # ragged M on the capped grid and below it, both 16-bit types, both ends of

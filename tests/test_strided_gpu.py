@@ -117,7 +117,12 @@ def test_fused_bwd_strided(name, M, N, dt, pads):
     assert gaps_untouched(dxbuf, N)
 
 
-@pytest.mark.parametrize("name,M,N,dt,pads", BWD_CASES[::2], ids=[c[0] for c in BWD_CASES[::2]])
+# the plain forward's 256-thread groups (rows of 4104-6144 16-bit elements
+# from 4096 rows), on padded rows
+FWD_CASES = BWD_CASES[::2] + [("4097x5120_bf16_half_rows", 4097, 5120, "bf16", (8, 16, 24, 8))]
+
+
+@pytest.mark.parametrize("name,M,N,dt,pads", FWD_CASES, ids=[c[0] for c in FWD_CASES])
 def test_forward_strided(name, M, N, dt, pads):
     print("case strided fwd", name, flush=True)
     td = T[dt]
