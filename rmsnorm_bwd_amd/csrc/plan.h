@@ -244,6 +244,10 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //                    block, for the plain forward's rows of 513-768 chunks
 //                    (4104-6144 elements; the plan has two a thread on 512
 //                    threads) from 4096 rows;
+//   FR_QUARTER_ROWS  three chunks a thread on 128-thread groups, four rows a
+//                    block, for rows of 257-384 chunks (2056-3072 elements;
+//                    the plan has one a thread on 512 threads) of every
+//                    forward from 3072 rows;
 //   FR_PLAN          the row plan as planned (everything else).
 // Measured on MI355X, GPU time per call, bf16 unless stated:
 //   three chunks: LayerNorm 4096 x 12288 42.8-43.1 -> 39.6-40.0 us, 1024 x
@@ -268,7 +272,21 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //   30.4-30.9 -> 28.7-29.1 but 16384 x 6144 131.4-132.3 -> 135.0-135.3) and
 //   LayerNorm's (4096 x 5120 19.6-19.8 -> 20.4-20.8, 1024 x 6144 7.6 -> 8.9)
 //   keep the plan.
-enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2 };
+//   quarter rows: plain 4096 x 2560 10.7-10.8 -> 9.0-9.1 us, 16384 x 2560
+//   34.4-34.5 -> 29.6-29.7, 32768 x 2560 65.5-65.7 -> 56.4-56.5, 16384 x
+//   3072 37.0-37.2 -> 34.7-34.9, 3072 x 3072 9.7 -> 7.7-7.8, 8192 x 2056
+//   18.5-19.0 -> 14.2-14.3, f16 4096 x 2816 11.2-11.4 -> 9.8-9.9; fused
+//   16384 x 2560 64.5-64.8 -> 56.4-56.5, 4096 x 3072 20.6-20.8 -> 17.1-17.2,
+//   3072 x 2560 14.2-14.3 -> 13.3-13.4, 8192 x 2304 33.1-33.6 -> 26.7-26.9,
+//   16384 x 3072 70.8-71.1 -> 67.2-67.5; LayerNorm 16384 x 2560 43.5-45.0 ->
+//   35.5-35.7, 4096 x 3072 13.7-13.8 -> 12.9-13.0, 3072 x 2560 11.2-11.5 ->
+//   10.1-10.2, f16 16384 x 3072 48.1-49.6 -> 39.2-39.7. With fewer rows the
+//   blocks hold fewer windows: 2048 rows even to slower (fused 2048 x 2560
+//   10.0-10.1 -> 10.4-10.5, 2048 x 3072 11.0-11.1 -> 11.4), 1024 rows
+//   slower (fused 1024 x 2560 5.7 -> 7.3, LayerNorm 1024 x 3072 5.7-5.9 ->
+//   6.3-6.4). The backward on the same groups loses (plain 16384 x 2560
+//   44.4-44.7 -> 48.8-49.0 us, 4096 x 2560 15.7-16.0 -> 20.3-20.6).
+enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3 };
 inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
     if (esize != 2 || p.long_row || p.vec != vw || p.tpr != RMSN_TPR_MAX) return FR_PLAN;
@@ -276,6 +294,8 @@ inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
         return FR_THREE_CHUNKS;
     if (p.k == 2 && N <= (int64_t)3 * (RMSN_TPR_MAX / 2) * vw && !fused && !layer && M >= 4096)
         return FR_HALF_ROWS;
+    if (p.k == 1 && N > (int64_t)(RMSN_TPR_MAX / 2) * vw && N <= (int64_t)3 * (RMSN_TPR_MAX / 4) * vw && M >= 3072)
+        return FR_QUARTER_ROWS;
     return FR_PLAN;
 }
 

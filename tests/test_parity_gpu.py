@@ -330,6 +330,22 @@ def test_plain_forward_half_row_groups(M, N, dt):
     check_case(plain_case(workloads.custom("plain", M, N, dt, 1e-6, seed=M + 5 * N)))
 
 
+# Every forward runs 16-bit rows of 2056-3072 elements on 128-thread groups
+# (three chunks a thread, four rows a block) from 3072 rows: M not a multiple
+# of four (a ragged last window), both 16-bit types, both ends of the range,
+# and 3071 rows (the plan's one chunk on 512 threads). The backward of each
+# runs too.
+QUARTER_ROWS = [("plain", 3072, 2560, "bf16"), ("plain", 4097, 2056, "f16"), ("fused", 3074, 3072, "bf16"),
+                ("fused", 4099, 2304, "f16"), ("plain", 3071, 3072, "bf16"), ("fused", 3071, 2056, "bf16")]
+
+
+@pytest.mark.parametrize("op,M,N,dt", QUARTER_ROWS)
+def test_forward_quarter_row_groups(op, M, N, dt):
+    _say("case forward quarter rows", op, M, N, dt)
+    w = workloads.custom(op, M, N, dt, 1e-6, seed=M + 3 * N)
+    check_case(plain_case(w) if op == "plain" else fused_case(w))
+
+
 # The fused backward runs 16-bit rows of 12296-16384 elements on the
 # long-row kernel, which loads a block's next row during the current one:
 # ragged M on the capped grid and below it, both 16-bit types, both ends of
