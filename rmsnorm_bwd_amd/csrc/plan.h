@@ -248,6 +248,11 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //                    block, for rows of 257-384 chunks (2056-3072 elements;
 //                    the plan has one a thread on 512 threads) of every
 //                    forward from 3072 rows;
+//   FR_WAVE_ROWS     three chunks a thread on one wavefront a row, four rows
+//                    a block, for rows of 129-192 chunks (1032-1536
+//                    elements; the plan has one a thread on 256 threads) of
+//                    the plain and LayerNorm forwards, and of the fused
+//                    forward from 2048 rows;
 //   FR_PLAN          the row plan as planned (everything else).
 // Measured on MI355X, GPU time per call, bf16 unless stated:
 //   three chunks: LayerNorm 4096 x 12288 42.8-43.1 -> 39.6-40.0 us, 1024 x
@@ -286,10 +291,24 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //   slower (fused 1024 x 2560 5.7 -> 7.3, LayerNorm 1024 x 3072 5.7-5.9 ->
 //   6.3-6.4). The backward on the same groups loses (plain 16384 x 2560
 //   44.4-44.7 -> 48.8-49.0 us, 4096 x 2560 15.7-16.0 -> 20.3-20.6).
-enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3 };
+//   wave rows: plain 4096 x 1536 7.6 -> 6.0 us, 16384 x 1536 21.0-21.1 ->
+//   19.3-19.4, 65536 x 1536 74.3-75.3 -> 70.2-70.6, 32768 x 1280 34.3-35.3
+//   -> 30.6-30.8, 8192 x 1032 11.3-11.4 -> 8.1-8.2, 1024 x 1536 3.9 -> 3.5,
+//   one row of 1536 2.3 -> 2.1, f16 16384 x 1280 19.8-20.1 -> 16.4-16.5;
+//   LayerNorm 4096 x 1280 9.0-9.4 -> 5.6-5.7, 16384 x 1536 25.2-25.3 ->
+//   19.8-20.1, 65536 x 1536 86.5-89.4 -> 72.2-72.3, 1024 x 1536 4.3-4.4 ->
+//   3.8, 128 x 1536 3.2 -> 3.1; fused 4096 x 1280 10.1-10.3 -> 8.7-8.8,
+//   2048 x 1536 5.9-6.0 -> 5.7-5.8, 65536 x 1280 117.7-118.0 -> 115.8-116.7,
+//   but 512 x 1536 3.54-3.57 -> 3.72-3.75 and 128 x 1280 3.21-3.23 ->
+//   3.29-3.32.
+enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3, FR_WAVE_ROWS = 4 };
 inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
-    if (esize != 2 || p.long_row || p.vec != vw || p.tpr != RMSN_TPR_MAX) return FR_PLAN;
+    if (esize != 2 || p.long_row || p.vec != vw) return FR_PLAN;
+    if (p.tpr == RMSN_TPR_MAX / 2 && p.k == 1 && N > (int64_t)(RMSN_TPR_MAX / 4) * vw &&
+        N <= (int64_t)3 * 64 * vw && (!fused || M >= 2048))
+        return FR_WAVE_ROWS;
+    if (p.tpr != RMSN_TPR_MAX) return FR_PLAN;
     if (p.k == 4 && N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26)))
         return FR_THREE_CHUNKS;
     if (p.k == 2 && N <= (int64_t)3 * (RMSN_TPR_MAX / 2) * vw && !fused && !layer && M >= 4096)

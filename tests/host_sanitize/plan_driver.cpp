@@ -140,9 +140,12 @@ int main() {
             // groups for the plain forward's 16-bit rows of 4104-6144
             // elements from 4096 rows; three chunks of 128-thread groups for
             // every forward's 16-bit rows of 2056-3072 elements from 3072
-            // rows; in each case the chunks cover the row
-            for (int64_t M : {int64_t(1), int64_t(300), int64_t(3071), int64_t(3072), int64_t(4095), int64_t(4096),
-                              int64_t(5461), int64_t(5462), int64_t(8192), int64_t(1) << 20})
+            // rows; three chunks of one wavefront for 16-bit rows of
+            // 1032-1536 elements (the fused forward's from 2048 rows); in
+            // each case the chunks cover the row
+            for (int64_t M : {int64_t(1), int64_t(300), int64_t(2047), int64_t(2048), int64_t(3071), int64_t(3072),
+                              int64_t(4095), int64_t(4096), int64_t(5461), int64_t(5462), int64_t(8192),
+                              int64_t(1) << 20})
                 for (int v = 0; v < 3; ++v) {
                     const bool fused = v == 1, layer = v == 2;
                     const int r = fwd_route(esize, fused, layer, p, M, N);
@@ -166,6 +169,12 @@ int main() {
                     if (r == FR_QUARTER_ROWS)
                         CHECK((int64_t)3 * 128 * p.vec >= N && p.tpr == 512 && p.k == 1,
                               "quarter-row chunks do not cover N = %lld", (long long)N);
+                    CHECK((r == FR_WAVE_ROWS) == (b16v && N > 1024 && N <= 1536 && (!fused || M >= 2048)),
+                          "forward wave-row route at M %lld N %lld esize %d variant %d", (long long)M,
+                          (long long)N, esize, v);
+                    if (r == FR_WAVE_ROWS)
+                        CHECK((int64_t)3 * 64 * p.vec >= N && p.tpr == 256 && p.k == 1,
+                              "wave-row chunks do not cover N = %lld", (long long)N);
                 }
             // the forward's grid: at least one block, at most one per row
             // window and 512, the fused forward's smaller cap only on the

@@ -50,6 +50,8 @@ CASES = [
     ("3075x2560_bf16", 3075, 2560, "bf16", 1e-6),  # forward on 128-thread groups, ragged last window
     ("4098x3072_f16", 4098, 3072, "f16", 1e-6),  # forward on 128-thread groups, the longest such row
     ("3071x2056_bf16", 3071, 2056, "bf16", 1e-6),  # one row short: the forward keeps the plan
+    ("1023x1536_bf16", 1023, 1536, "bf16", 1e-6),  # forward on one wavefront a row, ragged last window
+    ("5x1032_f16", 5, 1032, "f16", 1e-6),  # forward on one wavefront a row, the shortest such row
     ("65x4100_f32", 65, 4100, "f32", 1e-6),  # fp32 LayerNorm keeps four chunks a thread here
     ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread, next-row kernel
     ("4099x12296_bf16", 4099, 12296, "bf16", 1e-6),  # next-row kernel, ragged M

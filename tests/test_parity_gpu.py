@@ -346,6 +346,22 @@ def test_forward_quarter_row_groups(op, M, N, dt):
     check_case(plain_case(w) if op == "plain" else fused_case(w))
 
 
+# The plain and LayerNorm forwards, and the fused one from 2048 rows, run
+# 16-bit rows of 1032-1536 elements on one wavefront a row (three chunks a
+# thread, four rows a block): one row, ragged M, both 16-bit types, both ends
+# of the range, and the fused forward one row short of 2048 (the plan's one
+# chunk on 256 threads). The backward of each runs too.
+WAVE_ROWS = [("plain", 1, 1536, "bf16"), ("plain", 4099, 1032, "f16"), ("plain", 301, 1280, "bf16"),
+             ("fused", 2048, 1536, "bf16"), ("fused", 2051, 1032, "f16"), ("fused", 2047, 1536, "bf16")]
+
+
+@pytest.mark.parametrize("op,M,N,dt", WAVE_ROWS)
+def test_forward_wave_row_groups(op, M, N, dt):
+    _say("case forward wave rows", op, M, N, dt)
+    w = workloads.custom(op, M, N, dt, 1e-6, seed=M + 9 * N)
+    check_case(plain_case(w) if op == "plain" else fused_case(w))
+
+
 # The fused backward runs 16-bit rows of 12296-16384 elements on the
 # long-row kernel, which loads a block's next row during the current one:
 # ragged M on the capped grid and below it, both 16-bit types, both ends of
