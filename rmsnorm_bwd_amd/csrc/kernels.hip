@@ -1050,8 +1050,8 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
 // The forward's route for 16-bit rows whose plan leaves chunk slots empty
 // (fwd_route in plan.h, with its measurements): three chunks a thread on 512
 // threads, on 256-thread groups two rows a block, on 128-thread groups four
-// rows a block, or on one wavefront a row, four rows a block; every other
-// forward takes its row plan.
+// rows a block, on one wavefront a row (four rows a block) or on 32-thread
+// groups (eight rows a block); every other forward takes its row plan.
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
@@ -1062,6 +1062,7 @@ static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hip
         case FR_HALF_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 2, 3>(a, grid, s);
         case FR_QUARTER_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 4, 3>(a, grid, s);
         case FR_WAVE_ROWS: return launch_fwd_cfg<DT, VW, 64, 3>(a, grid, s);
+        case FR_NARROW_ROWS: return launch_fwd_cfg<DT, VW, 32, 3>(a, grid, s);
         default: break;
         }
     }

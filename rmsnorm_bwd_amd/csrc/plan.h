@@ -253,6 +253,11 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //                    elements; the plan has one a thread on 256 threads) of
 //                    the plain and LayerNorm forwards, and of the fused
 //                    forward from 2048 rows;
+//   FR_NARROW_ROWS   three chunks a thread on 32-thread groups, eight rows a
+//                    block, for rows of 65-96 chunks (520-768 elements; the
+//                    plan has one a thread on 128 threads) of the LayerNorm
+//                    forward at any size, the plain one from 256 rows and
+//                    the fused one from 4096 rows;
 //   FR_PLAN          the row plan as planned (everything else).
 // Measured on MI355X, GPU time per call, bf16 unless stated:
 //   three chunks: LayerNorm 4096 x 12288 42.8-43.1 -> 39.6-40.0 us, 1024 x
@@ -301,13 +306,26 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //   2048 x 1536 5.9-6.0 -> 5.7-5.8, 65536 x 1280 117.7-118.0 -> 115.8-116.7,
 //   but 512 x 1536 3.54-3.57 -> 3.72-3.75 and 128 x 1280 3.21-3.23 ->
 //   3.29-3.32.
-enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3, FR_WAVE_ROWS = 4 };
+//   narrow rows: LayerNorm 16384 x 768 14.6-14.7 -> 10.7-10.8 us, 65536 x
+//   768 47.1-47.4 -> 36.7-36.8, 4096 x 640 5.6 -> 4.3, 1024 x 768 3.5 ->
+//   3.3, one row of 768 2.7 -> 2.4; plain 16384 x 768 11.8-12.0 ->
+//   9.9-10.0, 65536 x 768 38.0-38.4 -> 35.5-35.7, 4096 x 768 4.8 -> 4.1,
+//   2048 x 520 3.8-3.9 -> 3.3, f16 16384 x 768 11.9 -> 9.8-10.0, but 128 x
+//   768 2.7-2.8 -> 2.8-2.9; fused 16384 x 768 20.2-20.5 -> 19.0-19.1, 65536
+//   x 640 63.2-63.3 -> 58.1-58.2, 8192 x 768 10.6-10.8 -> 9.2-9.3, 4096 x
+//   768 5.9-6.0 -> 5.7-5.8, but 3072 x 640 4.7-4.8 -> 5.0, 2048 x 768
+//   4.2-4.3 -> 4.6.
+enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3, FR_WAVE_ROWS = 4,
+             FR_NARROW_ROWS = 5 };
 inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
     if (esize != 2 || p.long_row || p.vec != vw) return FR_PLAN;
     if (p.tpr == RMSN_TPR_MAX / 2 && p.k == 1 && N > (int64_t)(RMSN_TPR_MAX / 4) * vw &&
         N <= (int64_t)3 * 64 * vw && (!fused || M >= 2048))
         return FR_WAVE_ROWS;
+    if (p.tpr == RMSN_TPR_MAX / 4 && p.k == 1 && N > (int64_t)(RMSN_TPR_MAX / 8) * vw &&
+        N <= (int64_t)3 * 32 * vw && (layer || M >= (fused ? 4096 : 256)))
+        return FR_NARROW_ROWS;
     if (p.tpr != RMSN_TPR_MAX) return FR_PLAN;
     if (p.k == 4 && N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26)))
         return FR_THREE_CHUNKS;

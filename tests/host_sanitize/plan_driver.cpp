@@ -141,9 +141,12 @@ int main() {
             // elements from 4096 rows; three chunks of 128-thread groups for
             // every forward's 16-bit rows of 2056-3072 elements from 3072
             // rows; three chunks of one wavefront for 16-bit rows of
-            // 1032-1536 elements (the fused forward's from 2048 rows); in
-            // each case the chunks cover the row
-            for (int64_t M : {int64_t(1), int64_t(300), int64_t(2047), int64_t(2048), int64_t(3071), int64_t(3072),
+            // 1032-1536 elements (the fused forward's from 2048 rows); three
+            // chunks of 32-thread groups for 16-bit rows of 520-768 elements
+            // (LayerNorm's at every M, the plain forward's from 256 rows, the
+            // fused one's from 4096); in each case the chunks cover the row
+            for (int64_t M : {int64_t(1), int64_t(255), int64_t(256), int64_t(300), int64_t(2047), int64_t(2048),
+                              int64_t(3071), int64_t(3072),
                               int64_t(4095), int64_t(4096), int64_t(5461), int64_t(5462), int64_t(8192),
                               int64_t(1) << 20})
                 for (int v = 0; v < 3; ++v) {
@@ -175,6 +178,13 @@ int main() {
                     if (r == FR_WAVE_ROWS)
                         CHECK((int64_t)3 * 64 * p.vec >= N && p.tpr == 256 && p.k == 1,
                               "wave-row chunks do not cover N = %lld", (long long)N);
+                    CHECK((r == FR_NARROW_ROWS) ==
+                              (b16v && N > 512 && N <= 768 && (layer || M >= (fused ? 4096 : 256))),
+                          "forward narrow-row route at M %lld N %lld esize %d variant %d", (long long)M,
+                          (long long)N, esize, v);
+                    if (r == FR_NARROW_ROWS)
+                        CHECK((int64_t)3 * 32 * p.vec >= N && p.tpr == 128 && p.k == 1,
+                              "narrow-row chunks do not cover N = %lld", (long long)N);
                 }
             // the forward's grid: at least one block, at most one per row
             // window and 512, the fused forward's smaller cap only on the

@@ -52,6 +52,8 @@ CASES = [
     ("3071x2056_bf16", 3071, 2056, "bf16", 1e-6),  # one row short: the forward keeps the plan
     ("1023x1536_bf16", 1023, 1536, "bf16", 1e-6),  # forward on one wavefront a row, ragged last window
     ("5x1032_f16", 5, 1032, "f16", 1e-6),  # forward on one wavefront a row, the shortest such row
+    ("1x768_bf16", 1, 768, "bf16", 1e-6),  # forward on 32-thread groups, one row
+    ("1031x520_f16", 1031, 520, "f16", 1e-6),  # forward on 32-thread groups, ragged last window
     ("65x4100_f32", 65, 4100, "f32", 1e-6),  # fp32 LayerNorm keeps four chunks a thread here
     ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread, next-row kernel
     ("4099x12296_bf16", 4099, 12296, "bf16", 1e-6),  # next-row kernel, ragged M

@@ -362,6 +362,22 @@ def test_forward_wave_row_groups(op, M, N, dt):
     check_case(plain_case(w) if op == "plain" else fused_case(w))
 
 
+# The forwards run 16-bit rows of 520-768 elements on 32-thread groups (three
+# chunks a thread, eight rows a block): the plain one from 256 rows, the
+# fused one from 4096 rows; M not a multiple of eight, both 16-bit types,
+# both ends of the range, and one row short of each limit (the plan's one
+# chunk on 128 threads). The backward of each runs too.
+NARROW_ROWS = [("plain", 256, 768, "bf16"), ("plain", 4099, 520, "f16"), ("plain", 255, 768, "bf16"),
+               ("fused", 4096, 768, "bf16"), ("fused", 4101, 640, "f16"), ("fused", 4095, 768, "bf16")]
+
+
+@pytest.mark.parametrize("op,M,N,dt", NARROW_ROWS)
+def test_forward_narrow_row_groups(op, M, N, dt):
+    _say("case forward narrow rows", op, M, N, dt)
+    w = workloads.custom(op, M, N, dt, 1e-6, seed=M + 17 * N)
+    check_case(plain_case(w) if op == "plain" else fused_case(w))
+
+
 # The fused backward runs 16-bit rows of 12296-16384 elements on the
 # long-row kernel, which loads a block's next row during the current one:
 # ragged M on the capped grid and below it, both 16-bit types, both ends of

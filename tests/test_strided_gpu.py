@@ -119,10 +119,12 @@ def test_fused_bwd_strided(name, M, N, dt, pads):
 
 # the plain forward's 256-thread groups (rows of 4104-6144 16-bit elements
 # from 4096 rows) and the forwards' 128-thread groups (2056-3072 elements from
-# 3072 rows) and single wavefronts (1032-1536 elements), on padded rows
+# 3072 rows), single wavefronts (1032-1536 elements) and 32-thread groups
+# (520-768 elements), on padded rows
 FWD_CASES = BWD_CASES[::2] + [("4097x5120_bf16_half_rows", 4097, 5120, "bf16", (8, 16, 24, 8)),
                               ("3073x2560_bf16_quarter_rows", 3073, 2560, "bf16", (16, 8, 8, 24)),
-                              ("2049x1280_bf16_wave_rows", 2049, 1280, "bf16", (8, 24, 16, 8))]
+                              ("2049x1280_bf16_wave_rows", 2049, 1280, "bf16", (8, 24, 16, 8)),
+                              ("301x768_bf16_narrow_rows", 301, 768, "bf16", (8, 8, 24, 16))]
 
 
 @pytest.mark.parametrize("name,M,N,dt,pads", FWD_CASES, ids=[c[0] for c in FWD_CASES])
@@ -157,7 +159,8 @@ def test_forward_strided(name, M, N, dt, pads):
 LN_CASES = BWD_CASES[:5] + [("300x14336_bf16_next_row", 300, 14336, "bf16", (8, 16, 24, 8)),
                             ("130x10240_bf16_three_chunks", 130, 10240, "bf16", (8, 24, 16, 8)),
                             ("3074x3072_bf16_quarter_rows", 3074, 3072, "bf16", (24, 8, 16, 8)),
-                            ("130x1536_bf16_wave_rows", 130, 1536, "bf16", (8, 16, 8, 24))]
+                            ("130x1536_bf16_wave_rows", 130, 1536, "bf16", (8, 16, 8, 24)),
+                            ("70x640_bf16_narrow_rows", 70, 640, "bf16", (16, 8, 24, 8))]
 
 
 @pytest.mark.parametrize("name,M,N,dt,pads", LN_CASES, ids=[c[0] for c in LN_CASES])
