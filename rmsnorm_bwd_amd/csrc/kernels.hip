@@ -1056,15 +1056,17 @@ template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
     constexpr int VW = 16 / ElemSize<DT>::value;
-    if constexpr (VW == 8) {
-        switch (fwd_route(ElemSize<DT>::value, a.residual != nullptr, a.mean != nullptr, p, a.M, a.N)) {
-        case FR_THREE_CHUNKS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX, 3>(a, grid, s);
-        case FR_HALF_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 2, 3>(a, grid, s);
-        case FR_QUARTER_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 4, 3>(a, grid, s);
-        case FR_WAVE_ROWS: return launch_fwd_cfg<DT, VW, 64, 3>(a, grid, s);
-        case FR_NARROW_ROWS: return launch_fwd_cfg<DT, VW, 32, 3>(a, grid, s);
-        default: break;
-        }
+    switch (fwd_route(ElemSize<DT>::value, a.residual != nullptr, a.mean != nullptr, p, a.M, a.N)) {
+    case FR_THREE_CHUNKS:  // 16-bit rows only
+        if constexpr (VW == 8) return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX, 3>(a, grid, s);
+        break;
+    case FR_HALF_ROWS:  // 16-bit rows only
+        if constexpr (VW == 8) return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 2, 3>(a, grid, s);
+        break;
+    case FR_QUARTER_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 4, 3>(a, grid, s);
+    case FR_WAVE_ROWS: return launch_fwd_cfg<DT, VW, 64, 3>(a, grid, s);
+    case FR_NARROW_ROWS: return launch_fwd_cfg<DT, VW, 32, 3>(a, grid, s);
+    default: break;
     }
     return dispatch<FwdLaunch, DT>(p, a, grid, s);
 }

@@ -259,6 +259,9 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //                    forward at any size, the plain one from 256 rows and
 //                    the fused one from 4096 rows;
 //   FR_PLAN          the row plan as planned (everything else).
+// The row lengths above are 16-bit elements; the fp32 LayerNorm forward takes
+// the wave, quarter and narrow routes too at the same chunk counts (516-768,
+// 1028-1536 and 260-384 fp32 elements), with LayerNorm's limits.
 // Measured on MI355X, GPU time per call, bf16 unless stated:
 //   three chunks: LayerNorm 4096 x 12288 42.8-43.1 -> 39.6-40.0 us, 1024 x
 //   12288 14.4-14.5 -> 13.1-13.2, 4096 x 10240 39.4 -> 36.2-36.4, 16384 x
@@ -315,11 +318,19 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //   x 640 63.2-63.3 -> 58.1-58.2, 8192 x 768 10.6-10.8 -> 9.2-9.3, 4096 x
 //   768 5.9-6.0 -> 5.7-5.8, but 3072 x 640 4.7-4.8 -> 5.0, 2048 x 768
 //   4.2-4.3 -> 4.6.
+//   fp32 LayerNorm: 4096 x 768 8.3-8.4 -> 6.7-7.0 us, 16384 x 768 23.1-23.3
+//   -> 19.7-19.8, 65536 x 768 80.9-82.0 -> 73.0-73.4, 128 x 768 2.9-3.1 ->
+//   2.7-2.9, one row of 640 2.5 -> 2.3 (wave rows); 16384 x 1536 42.7-43.0
+//   -> 37.2-37.3, 8192 x 1028 22.4-22.7 -> 17.4-17.5, 3072 x 1536 10.4-10.5
+//   -> 8.5 (quarter rows); 16384 x 384 13.1 -> 11.0, 1024 x 384 3.4 -> 3.35
+//   (narrow rows). The fp32 plain and fused forwards measured within 3%
+//   either way (plain 4096 x 1536 10.8-10.9 -> 11.0-11.2, fused 16384 x
+//   1536 67.9-68.2 -> 68.1-68.3) and keep the plan.
 enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3, FR_WAVE_ROWS = 4,
              FR_NARROW_ROWS = 5 };
 inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
-    if (esize != 2 || p.long_row || p.vec != vw) return FR_PLAN;
+    if (p.long_row || p.vec != vw || (esize != 2 && !layer)) return FR_PLAN;
     if (p.tpr == RMSN_TPR_MAX / 2 && p.k == 1 && N > (int64_t)(RMSN_TPR_MAX / 4) * vw &&
         N <= (int64_t)3 * 64 * vw && (!fused || M >= 2048))
         return FR_WAVE_ROWS;
@@ -327,7 +338,7 @@ inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
         N <= (int64_t)3 * 32 * vw && (layer || M >= (fused ? 4096 : 256)))
         return FR_NARROW_ROWS;
     if (p.tpr != RMSN_TPR_MAX) return FR_PLAN;
-    if (p.k == 4 && N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26)))
+    if (esize == 2 && p.k == 4 && N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26)))
         return FR_THREE_CHUNKS;
     if (p.k == 2 && N <= (int64_t)3 * (RMSN_TPR_MAX / 2) * vw && !fused && !layer && M >= 4096)
         return FR_HALF_ROWS;

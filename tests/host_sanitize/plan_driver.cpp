@@ -166,20 +166,27 @@ int main() {
                     if (r == FR_HALF_ROWS)
                         CHECK((int64_t)3 * 256 * p.vec >= N && p.tpr == 512 && p.k == 2,
                               "half-row chunks do not cover N = %lld", (long long)N);
-                    CHECK((r == FR_QUARTER_ROWS) == (b16v && N > 2048 && N <= 3072 && M >= 3072),
+                    CHECK((r == FR_QUARTER_ROWS) ==
+                              (p.vec == 16 / esize && (esize == 2 || layer) && N > 256 * (16 / esize) &&
+                               N <= 384 * (16 / esize) && M >= 3072),
                           "forward quarter-row route at M %lld N %lld esize %d variant %d", (long long)M,
                           (long long)N, esize, v);
                     if (r == FR_QUARTER_ROWS)
                         CHECK((int64_t)3 * 128 * p.vec >= N && p.tpr == 512 && p.k == 1,
                               "quarter-row chunks do not cover N = %lld", (long long)N);
-                    CHECK((r == FR_WAVE_ROWS) == (b16v && N > 1024 && N <= 1536 && (!fused || M >= 2048)),
+                    // the fp32 LayerNorm forward takes the wave, quarter and
+                    // narrow routes at the same chunk counts
+                    const int vwd = 16 / esize;
+                    const bool elig = p.vec == vwd && (esize == 2 || layer);
+                    CHECK((r == FR_WAVE_ROWS) ==
+                              (elig && N > 128 * vwd && N <= 192 * vwd && (!fused || M >= 2048)),
                           "forward wave-row route at M %lld N %lld esize %d variant %d", (long long)M,
                           (long long)N, esize, v);
                     if (r == FR_WAVE_ROWS)
                         CHECK((int64_t)3 * 64 * p.vec >= N && p.tpr == 256 && p.k == 1,
                               "wave-row chunks do not cover N = %lld", (long long)N);
                     CHECK((r == FR_NARROW_ROWS) ==
-                              (b16v && N > 512 && N <= 768 && (layer || M >= (fused ? 4096 : 256))),
+                              (elig && N > 64 * vwd && N <= 96 * vwd && (layer || M >= (fused ? 4096 : 256))),
                           "forward narrow-row route at M %lld N %lld esize %d variant %d", (long long)M,
                           (long long)N, esize, v);
                     if (r == FR_NARROW_ROWS)

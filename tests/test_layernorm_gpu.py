@@ -54,6 +54,10 @@ CASES = [
     ("5x1032_f16", 5, 1032, "f16", 1e-6),  # forward on one wavefront a row, the shortest such row
     ("1x768_bf16", 1, 768, "bf16", 1e-6),  # forward on 32-thread groups, one row
     ("1031x520_f16", 1031, 520, "f16", 1e-6),  # forward on 32-thread groups, ragged last window
+    ("1x640_f32", 1, 640, "f32", 1e-6),  # fp32 forward on one wavefront a row
+    ("3073x1536_f32", 3073, 1536, "f32", 1e-6),  # fp32 forward on 128-thread groups, ragged last window
+    ("130x384_f32", 130, 384, "f32", 1e-6),  # fp32 forward on 32-thread groups
+    ("3071x1028_f32", 3071, 1028, "f32", 1e-6),  # one row short: the fp32 forward keeps the plan
     ("65x4100_f32", 65, 4100, "f32", 1e-6),  # fp32 LayerNorm keeps four chunks a thread here
     ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread, next-row kernel
     ("4099x12296_bf16", 4099, 12296, "bf16", 1e-6),  # next-row kernel, ragged M
