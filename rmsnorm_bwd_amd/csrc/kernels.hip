@@ -1050,8 +1050,9 @@ static hipError_t dispatch_bwd(const RowPlan &p, const BwdArgs &a, int grid, hip
 // The forward's route for 16-bit rows whose plan leaves chunk slots empty
 // (fwd_route in plan.h, with its measurements): three chunks a thread on 512
 // threads, on 256-thread groups two rows a block, on 128-thread groups four
-// rows a block, on one wavefront a row (four rows a block) or on 32-thread
-// groups (eight rows a block); every other forward takes its row plan.
+// rows a block, on one wavefront a row (four rows a block), on 32-thread
+// groups (eight rows a block) or with three chunks instead of four on the
+// plan's 16-thread groups; every other forward takes its row plan.
 template <int DT>
 static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hipStream_t s) {
     if (p.long_row) return launch_fwd_long(DT, p, a, grid, s);
@@ -1066,6 +1067,9 @@ static hipError_t dispatch_fwd(const RowPlan &p, const FwdArgs &a, int grid, hip
     case FR_QUARTER_ROWS: return launch_fwd_cfg<DT, VW, RMSN_TPR_MAX / 4, 3>(a, grid, s);
     case FR_WAVE_ROWS: return launch_fwd_cfg<DT, VW, 64, 3>(a, grid, s);
     case FR_NARROW_ROWS: return launch_fwd_cfg<DT, VW, 32, 3>(a, grid, s);
+    case FR_SHORT_ROWS:  // 16-bit rows only
+        if constexpr (VW == 8) return launch_fwd_cfg<DT, VW, 16, 3>(a, grid, s);
+        break;
     default: break;
     }
     return dispatch<FwdLaunch, DT>(p, a, grid, s);

@@ -258,6 +258,9 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //                    plan has one a thread on 128 threads) of the LayerNorm
 //                    forward at any size, the plain one from 256 rows and
 //                    the fused one from 4096 rows;
+//   FR_SHORT_ROWS    three chunks a thread on the plan's 16-thread groups
+//                    (sixteen rows a block) instead of four, for 16-bit rows
+//                    of 33-48 chunks (264-384 elements) of every forward;
 //   FR_PLAN          the row plan as planned (everything else).
 // The row lengths above are 16-bit elements; the fp32 LayerNorm forward takes
 // the wave, quarter and narrow routes too at the same chunk counts (516-768,
@@ -326,8 +329,13 @@ inline int bwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
 //   (narrow rows). The fp32 plain and fused forwards measured within 3%
 //   either way (plain 4096 x 1536 10.8-10.9 -> 11.0-11.2, fused 16384 x
 //   1536 67.9-68.2 -> 68.1-68.3) and keep the plan.
+//   short rows: plain 16384 x 384 6.2 -> 5.9 us, 65536 x 384 19.0-19.2 ->
+//   18.8-19.0, 131072 x 320 30.9-31.1 -> 30.4-30.5, 1024 x 384 3.2 -> 3.0;
+//   LayerNorm 16384 x 384 6.2-6.3 -> 5.8, 65536 x 384 20.6-20.7 ->
+//   19.5-19.7, 1024 x 384 3.4-3.5 -> 3.2; fused 16384 x 320 8.9-9.0 ->
+//   8.5-8.6, 65536 x 384 35.6-35.7 -> 35.7.
 enum : int { FR_PLAN = 0, FR_THREE_CHUNKS = 1, FR_HALF_ROWS = 2, FR_QUARTER_ROWS = 3, FR_WAVE_ROWS = 4,
-             FR_NARROW_ROWS = 5 };
+             FR_NARROW_ROWS = 5, FR_SHORT_ROWS = 6 };
 inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_t M, int64_t N) {
     const int vw = 16 / esize;
     if (p.long_row || p.vec != vw || (esize != 2 && !layer)) return FR_PLAN;
@@ -337,6 +345,7 @@ inline int fwd_route(int esize, bool fused, bool layer, const RowPlan &p, int64_
     if (p.tpr == RMSN_TPR_MAX / 4 && p.k == 1 && N > (int64_t)(RMSN_TPR_MAX / 8) * vw &&
         N <= (int64_t)3 * 32 * vw && (layer || M >= (fused ? 4096 : 256)))
         return FR_NARROW_ROWS;
+    if (esize == 2 && p.tpr == 16 && p.k == 4 && N <= (int64_t)3 * 16 * vw) return FR_SHORT_ROWS;
     if (p.tpr != RMSN_TPR_MAX) return FR_PLAN;
     if (esize == 2 && p.k == 4 && N <= (int64_t)3 * RMSN_TPR_MAX * vw && (layer || M * N <= (int64_t(1) << 26)))
         return FR_THREE_CHUNKS;

@@ -144,7 +144,9 @@ int main() {
             // 1032-1536 elements (the fused forward's from 2048 rows); three
             // chunks of 32-thread groups for 16-bit rows of 520-768 elements
             // (LayerNorm's at every M, the plain forward's from 256 rows, the
-            // fused one's from 4096); in each case the chunks cover the row
+            // fused one's from 4096); three chunks instead of four on
+            // 16-thread groups for 16-bit rows of 264-384 elements; in each
+            // case the chunks cover the row
             for (int64_t M : {int64_t(1), int64_t(255), int64_t(256), int64_t(300), int64_t(2047), int64_t(2048),
                               int64_t(3071), int64_t(3072),
                               int64_t(4095), int64_t(4096), int64_t(5461), int64_t(5462), int64_t(8192),
@@ -189,6 +191,12 @@ int main() {
                               (elig && N > 64 * vwd && N <= 96 * vwd && (layer || M >= (fused ? 4096 : 256))),
                           "forward narrow-row route at M %lld N %lld esize %d variant %d", (long long)M,
                           (long long)N, esize, v);
+                    CHECK((r == FR_SHORT_ROWS) == (b16v && N > 256 && N <= 384),
+                          "forward short-row route at M %lld N %lld esize %d variant %d", (long long)M,
+                          (long long)N, esize, v);
+                    if (r == FR_SHORT_ROWS)
+                        CHECK((int64_t)3 * 16 * p.vec >= N && p.tpr == 16 && p.k == 4,
+                              "short-row chunks do not cover N = %lld", (long long)N);
                     if (r == FR_NARROW_ROWS)
                         CHECK((int64_t)3 * 32 * p.vec >= N && p.tpr == 128 && p.k == 1,
                               "narrow-row chunks do not cover N = %lld", (long long)N);

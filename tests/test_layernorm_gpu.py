@@ -58,6 +58,7 @@ CASES = [
     ("3073x1536_f32", 3073, 1536, "f32", 1e-6),  # fp32 forward on 128-thread groups, ragged last window
     ("130x384_f32", 130, 384, "f32", 1e-6),  # fp32 forward on 32-thread groups
     ("3071x1028_f32", 3071, 1028, "f32", 1e-6),  # one row short: the fp32 forward keeps the plan
+    ("1025x384_bf16", 1025, 384, "bf16", 1e-6),  # forward with three chunks on 16-thread groups
     ("65x4100_f32", 65, 4100, "f32", 1e-6),  # fp32 LayerNorm keeps four chunks a thread here
     ("40x12296_bf16", 40, 12296, "bf16", 1e-6),  # one chunk past: four chunks a thread, next-row kernel
     ("4099x12296_bf16", 4099, 12296, "bf16", 1e-6),  # next-row kernel, ragged M

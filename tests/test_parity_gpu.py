@@ -378,6 +378,22 @@ def test_forward_narrow_row_groups(op, M, N, dt):
     check_case(plain_case(w) if op == "plain" else fused_case(w))
 
 
+# Every forward runs 16-bit rows of 264-384 elements with three chunks a
+# thread instead of four on 16-thread groups (sixteen rows a block): one row,
+# M not a multiple of sixteen, both 16-bit types, both ends of the range, and
+# 392 elements (one chunk past: four chunks a thread). The backward of each
+# runs too.
+SHORT_ROWS = [("plain", 1, 384, "bf16"), ("plain", 4099, 264, "f16"), ("plain", 300, 392, "bf16"),
+              ("fused", 300, 320, "bf16"), ("fused", 17, 384, "f16")]
+
+
+@pytest.mark.parametrize("op,M,N,dt", SHORT_ROWS)
+def test_forward_short_rows_three_chunks(op, M, N, dt):
+    _say("case forward short rows", op, M, N, dt)
+    w = workloads.custom(op, M, N, dt, 1e-6, seed=M + 19 * N)
+    check_case(plain_case(w) if op == "plain" else fused_case(w))
+
+
 # The fused backward runs 16-bit rows of 12296-16384 elements on the
 # long-row kernel, which loads a block's next row during the current one:
 # ragged M on the capped grid and below it, both 16-bit types, both ends of
