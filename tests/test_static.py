@@ -8,13 +8,16 @@ import py_compile
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SKIP_DIRS = {"_work", "gpurun_out", ".git", "__pycache__", "build", "_build", ".pytest_cache"}
+def _skip(name):
+    """Folders that hold no committed sources: working and cache folders (a
+    leading underscore or dot), run outputs (a trailing "_out") and builds."""
+    return name.startswith(("_", ".")) or name.endswith("_out") or name == "build"
 
 
 def _sources():
     out = []
     for d, dirs, files in os.walk(ROOT):
-        dirs[:] = [x for x in dirs if x not in SKIP_DIRS and not x.startswith(".")]
+        dirs[:] = [x for x in dirs if not _skip(x)]
         out += [os.path.join(d, f) for f in files if f.endswith(".py")]
     return sorted(out)
 
